@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused fp16 GEMM + scale + ReLU on one MI355X.
+
+A step is one call of the whole operation, C = ReLU(alpha * A @ B), on one
+batch of synthetic fp16 input already resident in HBM.  Timing follows the
+tutorial's benchmark helper (PKUHPC scow-tutorial "Tutorial14", section 2:
+warm-up calls, a synchronise, an event, the timed calls, an event, a
+synchronise, mean time per call, TFLOP/s = 2*M*N*K / time), with the events
+recorded on the stream the kernels are launched on.  By default the K timed
+calls are captured once into a HIP graph and the graph is replayed, so host
+launch overhead does not pace the GPU; --launch eager issues them one by one.
+
+Prints one JSON line on stdout.  Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "square_1024"
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Digest of the kernel and launch sources; a traffic measurement taken
+    on other sources is stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, flops: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, a, b, target_s: float):
+    """The oracle, as it is, on a bounded sample of the same workload: the
+    first R rows of A against all of B, R sized for about `target_s` seconds."""
+    from oracle import oracle
+    from tiled_dense_gemm_scale_amd import workloads as W
+
+    orc = oracle.load()
+    threads = oracle.default_threads()
+    a_bits = W.fp16_bits(a)
+    b_bits = W.fp16_bits(b)
+    # calibrate on a few rows, then size the sample
+    rows = min(w.M, max(threads, 8))
+    t0 = time.perf_counter()
+    orc.gemm_scale_relu(a_bits[:rows], b_bits, w.alpha, nthreads=threads)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / rows
+    R = int(min(w.M, max(rows, target_s / max(per_row, 1e-9))))
+    R = max(threads, (R // threads) * threads) if R < w.M else w.M
+    t0 = time.perf_counter()
+    orc.gemm_scale_relu(a_bits[:R], b_bits, w.alpha, nthreads=threads)
+    t = time.perf_counter() - t0
+    flops = 2.0 * R * w.N * w.K
+    return {
+        "value": round(flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{R - 1} of C ({R}x{w.N} outputs, K={w.K}), full fp64 oracle, {t:.2f} s",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--config-id", type=int, default=-1, help="force a tile configuration")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import tiled_dense_gemm_scale_amd as gsr
+    from tiled_dense_gemm_scale_amd import workloads as W
+
+    if args.workload == W.SKINNY.name:
+        w = W.SKINNY
+    else:
+        w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    log(f"[bench] workload {w.name}: {w.note}")
+
+    a_cpu, b_cpu = W.workload_inputs(w)
+    a = a_cpu.to(dev)
+    b = b_cpu.to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    cfg = gsr.select_config(w.M, w.N, w.K) if args.config_id < 0 else gsr.get_config(args.config_id)
+    log(f"[bench] tile config {cfg}")
+
+    def step():
+        gsr.gemm_scale_relu_ex(a, b, w.alpha, args.config_id, c=c, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()  # single rank: the barrier is this synchronise
+    start.record(stream)
+    if graph is not None:
+        with torch.cuda.stream(stream):
+            graph.replay()
+    else:
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    ms = elapsed_ms / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps in {elapsed_ms:.3f} ms -> {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_FP16_TFLOPS:.1f}% of {PEAK_FP16_TFLOPS})")
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 1024 * 1024 // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n * 2} bytes read, {n * 2} bytes written")
+
+    traffic = load_traffic(w.name, w.flops)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(tflops, 3),
+        "peak": PEAK_FP16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "traffic": traffic,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds)
+        log(f"[bench] cpu_baseline {cpu}")
+
+    out = {
+        "metric": "TFLOP/s and % of dense fp16 MFMA peak for fused GEMM+scale+ReLU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
+            "inputs": f"seed 0 randn fp32 -> fp16, A then B, B std {w.b_std:g}",
+            "launch": args.launch,
+            "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n")},
+            "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
+            "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,103 @@
+/*
+ * gsr.h -- C ABI of the fused fp16 GEMM + scale + ReLU library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (PKUHPC scow-tutorial "Tutorial14: 使用TileLang语言编写attention
+ * 算子", section 3 "算子介绍", display formula and symbol list; the kernel
+ * listing in section 2 "编写算子" fixes the types and the epilogue order):
+ *
+ *     C[m,n] = ReLU( alpha * sum_{k<K} A[m,k] * B[k,n] ),  ReLU(x) = max(x, 0)
+ *
+ *   A  M x K, IEEE binary16, row-major (leading dimension K)
+ *   B  K x N, IEEE binary16, row-major (leading dimension N)
+ *   C  M x N, IEEE binary16, row-major (leading dimension N), written once
+ *   alpha  binary32 scalar
+ * Products are accumulated in binary32; the scale and the max(., 0) are applied
+ * to the binary32 sum in registers and the result is narrowed to binary16 with
+ * round-to-nearest-even on the single store.  Non-positive results are +0.
+ *
+ * Ownership and ordering.  A, B and C are device pointers owned by the caller
+ * (any allocation the HIP runtime can address from the current device).  The
+ * library allocates nothing and keeps no per-call state; it only enqueues
+ * kernels on `stream` (a hipStream_t; NULL means the null stream) and returns
+ * before they finish.  The caller synchronises.  Calls are thread-safe.
+ *
+ * Error behaviour.  Arguments are checked on the host before anything is
+ * enqueued; a nonzero status means nothing was launched (except
+ * GSR_ERROR_LAUNCH, which reports a failed launch).  No status aborts the
+ * process.
+ */
+#ifndef GSR_H_
+#define GSR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gsr_status {
+    GSR_SUCCESS = 0,
+    /* a dimension < 0; a null or odd-address pointer where the extent is
+     * nonzero; C's byte range overlapping A's or B's; alpha not finite */
+    GSR_ERROR_INVALID_VALUE = 1,
+    /* a dimension >= 2^31, or a matrix of 2^31 bytes or more (the kernels
+     * use 32-bit byte offsets) */
+    GSR_ERROR_TOO_LARGE = 2,
+    GSR_ERROR_NO_DEVICE = 3,          /* no HIP device is visible */
+    GSR_ERROR_UNSUPPORTED_DEVICE = 4, /* the current device is not gfx950 */
+    GSR_ERROR_LAUNCH = 5,             /* the runtime rejected the launch */
+    GSR_ERROR_INVALID_CONFIG = 6      /* gemm_scale_relu_ex: unknown config id */
+};
+
+/* One compiled tile configuration.  A workgroup of waves_m*waves_n wave64s
+ * owns a block_m x block_n tile of C and walks K in steps of block_k through
+ * `stages` LDS buffers; each wave owns a (block_m/waves_m) x (block_n/waves_n)
+ * sub-tile built from 32x32x16 fp16 MFMAs.  group_m is the number of tile rows
+ * in one group of the grouped launch order, xcd_remap says whether workgroup
+ * ids are regrouped so that neighbouring tiles run on the same XCD. */
+typedef struct gsr_config {
+    int32_t id;
+    int32_t block_m, block_n, block_k;
+    int32_t waves_m, waves_n;
+    int32_t stages;
+    int32_t group_m;
+    int32_t xcd_remap;
+    int32_t lds_bytes;
+} gsr_config;
+
+/* The fused operation (the tutorial's kernel call: A, B, C, scale).
+ * M, N, K >= 0.  M == 0 or N == 0: success, nothing enqueued.  K == 0: every
+ * output is the empty sum, C is filled with +0.  Any pointer alignment of at
+ * least 2 bytes is accepted; 16-byte aligned A and B, 8-byte aligned C and
+ * K, N multiples of 8 take the 128-bit vector path, anything else an
+ * element-wise path of the same kernel.  Returns a gsr_status. */
+int gemm_scale_relu(int64_t M, int64_t N, int64_t K,
+                    const void* A, const void* B, void* C,
+                    float alpha, void* stream);
+
+/* As gemm_scale_relu with a forced tile configuration (config_id from
+ * gsr_get_config; -1 = the selector's choice).  For sweeps and tests. */
+int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K,
+                       const void* A, const void* B, void* C,
+                       float alpha, void* stream, int32_t config_id);
+
+/* The configuration the selector picks for an M x N x K problem.  Host only;
+ * touches no device.  Returns GSR_SUCCESS or GSR_ERROR_INVALID_VALUE. */
+int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out);
+
+/* Number of compiled tile configurations, and the description of one. */
+int gsr_num_configs(void);
+int gsr_get_config(int32_t config_id, gsr_config* out);
+
+/* A static, human-readable name for a status code. */
+const char* gsr_status_string(int status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int gsr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSR_H_ */

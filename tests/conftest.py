@@ -21,3 +21,13 @@ def orc():
     from oracle import oracle
 
     return oracle.load()
+
+
+@pytest.fixture(scope="session")
+def native():
+    """The C-ABI library (built in-tree with hipcc if it is not there yet)."""
+    from tiled_dense_gemm_scale_amd import _native, build
+
+    if not os.path.exists(_native.LIBRARY):
+        build.build()
+    return _native

@@ -1,0 +1,122 @@
+"""The C-ABI library on the host: it loads, exports every symbol that
+include/gsr.h declares, describes its tile table, and rejects bad arguments
+before touching any device.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsr.h")
+
+FAKE = 0x7F0000000000  # a 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gemm_scale_relu", "gemm_scale_relu_ex", "gsr_select_config", "gsr_num_configs",
+              "gsr_get_config", "gsr_status_string", "gsr_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(native):
+    lib = ctypes.CDLL(native.LIBRARY)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in gsr.h but not exported"
+
+
+def test_config_struct_layout(native):
+    assert ctypes.sizeof(native.GsrConfig) == 40
+
+
+def test_config_table(native):
+    n = native.num_configs()
+    assert n >= 4
+    for i in range(n):
+        c = native.get_config(i)
+        assert c["id"] == i
+        assert c["block_k"] == 64 and c["stages"] == 2
+        assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
+        lds = c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
+        assert c["lds_bytes"] == lds <= 163840
+    with pytest.raises(native.GsrError):
+        native.get_config(n)
+    with pytest.raises(native.GsrError):
+        native.get_config(-1)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (1024, 1024, 1024), (4096, 4096, 4096),
+                                   (4097, 11008, 4096), (16384, 16384, 16384), (16, 11008, 4096),
+                                   (1, 1, 1), (0, 5, 5)])
+def test_selector(native, shape):
+    c = native.select_config(*shape)
+    assert 0 <= c["id"] < native.num_configs()
+    M, N, _ = shape
+    if M * N >= 256 * 256 * 256:
+        # large problems use a tile that still yields one workgroup per CU
+        assert -(-M // c["block_m"]) * -(-N // c["block_n"]) >= 256
+
+
+def test_status_strings(native):
+    assert native.status_string(0) == "success"
+    for s in range(1, 7):
+        assert native.status_string(s) not in ("", "success", "unknown status")
+    assert native.status_string(99) == "unknown status"
+    assert native.version() >= 100
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, FAKE, FAKE + 4096, FAKE + 8192), 1),
+    ((4, -1, 4, FAKE, FAKE + 4096, FAKE + 8192), 1),
+    ((4, 4, -1, FAKE, FAKE + 4096, FAKE + 8192), 1),
+    ((4, 4, 4, 0, FAKE + 4096, FAKE + 8192), 1),        # null A
+    ((4, 4, 4, FAKE, 0, FAKE + 8192), 1),               # null B
+    ((4, 4, 4, FAKE, FAKE + 4096, 0), 1),               # null C
+    ((4, 4, 4, FAKE + 1, FAKE + 4096, FAKE + 8192), 1),  # odd A
+    ((4, 4, 4, FAKE, FAKE + 4097, FAKE + 8192), 1),      # odd B
+    ((4, 4, 4, FAKE, FAKE + 4096, FAKE + 8193), 1),      # odd C
+    ((4, 4, 4, FAKE, FAKE + 4096, FAKE + 16), 1),        # C overlaps A
+    ((4, 4, 4, FAKE, FAKE + 4096, FAKE + 4096 + 30), 1), # C overlaps B
+    ((2 ** 31, 4, 4, FAKE, FAKE + 4096, FAKE + 8192), 2),
+    ((40000, 40000, 8, FAKE, FAKE + 2 ** 32, FAKE + 2 ** 33), 2),  # C >= 2^31 bytes
+])
+def test_argument_errors(native, args, status):
+    M, N, K, A, B, C = args
+    assert native.gemm_scale_relu(M, N, K, A, B, C, 0.5, 0) == status
+
+
+def test_nonfinite_alpha_and_bad_config(native):
+    import math
+    assert native.gemm_scale_relu(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, math.nan, 0) == 1
+    assert native.gemm_scale_relu(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, math.inf, 0) == 1
+    assert native.gemm_scale_relu_ex(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, 0, 99) == 6
+    assert native.gemm_scale_relu_ex(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, 0, -2) == 6
+
+
+def test_empty_output_is_a_noop(native):
+    # M == 0 or N == 0: success, nothing enqueued, no device needed
+    assert native.gemm_scale_relu(0, 16, 16, 0, 0, 0, 0.5, 0) == 0
+    assert native.gemm_scale_relu(16, 0, 16, 0, 0, 0, 0.5, 0) == 0
+
+
+def test_no_device(native):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present")
+    assert native.gemm_scale_relu(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, 0) == 3
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    from tiled_dense_gemm_scale_amd import _native
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIBRARY", "/nonexistent/libgsr.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        _native.lib()

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Small and ragged shapes are checked on every output; the full-size
+workloads, in the launch configuration the benchmark times (the selector's
+choice), on 4096 sampled outputs plus any ragged edge row, and on
+properties that hold at any size.  Integer-valued inputs make the fp32 sums
+exact, so there the comparison is bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity as PT
+from tiled_dense_gemm_scale_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def gsr(native):
+    import tiled_dense_gemm_scale_amd as g
+
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return g
+
+
+def bits(t):
+    return W.fp16_bits(t)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["square_256", "square_1024"])
+def test_workload_full(gsr, orc, name):
+    w = W.WORKLOADS[name]
+    a, b = W.workload_inputs(w)
+    say(f"[gpu] {name} {w.M}x{w.N}x{w.K} alpha={w.alpha} selector")
+    got = PT.run_gpu(a, b, w.alpha)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), w.alpha)
+    PT.assert_parity(name, got, ref)
+
+
+@pytest.mark.parametrize("name", ["square_4096", "llm_mlp_4097x11008x4096", "square_16384"])
+def test_workload_sampled(gsr, orc, name):
+    w = W.WORKLOADS[name]
+    a, b = W.workload_inputs(w)
+    say(f"[gpu] {name} {w.M}x{w.N}x{w.K} alpha={w.alpha} selector, sampled")
+    got = PT.run_gpu(a, b, w.alpha)
+    extra = [w.M - 1] if w.M % 256 else []
+    ms, ns = W.sample_points(w.M, w.N, 4096, seed=1, extra_rows=extra)
+    ref, _ = orc.gemm_scale_relu_points(bits(a), bits(b), w.alpha, ms, ns)
+    PT.assert_parity(name + " (sampled)", got[ms, ns], ref, coords=(ms, ns))
+    # properties of the whole output: finite, non-negative, about half zeros
+    v = PT.f16(got)
+    assert np.all(np.isfinite(v))
+    assert not np.any(got & 0x8000), "negative or -0 output"
+    assert np.all(v >= 0)
+    zf = float(np.mean(got == 0))
+    assert 0.45 < zf < 0.55, zf
+
+
+# --------------------------------------------------------------------------
+# every tile configuration, several tiles and ragged tails
+# --------------------------------------------------------------------------
+
+RAGGED = [
+    (1, 1, 1),
+    (17, 33, 65),
+    (64, 64, 64),
+    (300, 520, 200),      # K multiple of 8, not of 64; 128-bit path
+    (257, 263, 129),      # N, K odd: element path
+    (513, 384, 1000),
+    (129, 1031, 72),      # N % 8 != 0: element path
+    (1000, 1500, 704),
+]
+
+
+def _configs(gsr):
+    return list(range(gsr.num_configs()))
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_every_config(gsr, orc, shape):
+    M, N, K = shape
+    a, b = W.normal_inputs(M, N, K, seed=M * 7 + N * 3 + K)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
+    for cid in [-1] + _configs(gsr):
+        say(f"[gpu] ragged {shape} config {cid}")
+        got = PT.run_gpu(a, b, 0.5, config_id=cid)
+        PT.assert_parity(f"{shape} cfg{cid}", got, ref)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 200), (257, 263, 129), (1024, 1024, 512),
+                                   (4097, 384, 256)], ids=lambda s: "x".join(map(str, s)))
+def test_integer_inputs_bitwise(gsr, orc, shape):
+    M, N, K = shape
+    a, b = W.integer_inputs(M, N, K, seed=5)
+    for alpha in (0.5, 1.0, -0.5):
+        ref, _ = orc.gemm_scale_relu(bits(a), bits(b), alpha)
+        for cid in [-1] + _configs(gsr):
+            say(f"[gpu] integer {shape} alpha={alpha} config {cid}")
+            got = PT.run_gpu(a, b, alpha, config_id=cid)
+            PT.assert_bitwise(f"integer {shape} alpha={alpha} cfg{cid}", got, ref)
+
+
+def test_integer_full_size_llm(gsr, orc):
+    """The LLM-MLP shape with integer inputs: bit-exact on sampled outputs and
+    the whole ragged last row."""
+    w = W.WORKLOADS["llm_mlp_4097x11008x4096"]
+    a, b = W.integer_inputs(w.M, w.N, w.K, seed=11, lo=-2, hi=2)
+    say("[gpu] integer llm shape")
+    got = PT.run_gpu(a, b, 0.5)
+    ms, ns = W.sample_points(w.M, w.N, 4096, seed=1, extra_rows=[w.M - 1])
+    ref, _ = orc.gemm_scale_relu_points(bits(a), bits(b), 0.5, ms, ns)
+    PT.assert_bitwise("integer llm sampled", got[ms, ns], ref)
+
+
+# --------------------------------------------------------------------------
+# edges, layout, guard bands
+# --------------------------------------------------------------------------
+
+def test_k_zero_fills_zero(gsr):
+    say("[gpu] K=0")
+    c = torch.full((37, 45), float("nan"), dtype=torch.float16, device=DEV)
+    a = torch.empty((37, 0), dtype=torch.float16, device=DEV)
+    b = torch.empty((0, 45), dtype=torch.float16, device=DEV)
+    gsr.gemm_scale_relu(a, b, 0.5, c=c)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0) and not torch.any(torch.signbit(c))
+
+
+def test_empty_outputs(gsr):
+    say("[gpu] M=0 / N=0")
+    a = torch.empty((0, 8), dtype=torch.float16, device=DEV)
+    b = torch.ones((8, 16), dtype=torch.float16, device=DEV)
+    assert gsr.gemm_scale_relu(a, b, 0.5).shape == (0, 16)
+    b2 = torch.ones((8, 0), dtype=torch.float16, device=DEV)
+    a2 = torch.ones((4, 8), dtype=torch.float16, device=DEV)
+    assert gsr.gemm_scale_relu(a2, b2, 0.5).shape == (4, 0)
+
+
+@pytest.mark.parametrize("offset", [1, 3, 8])
+def test_unaligned_pointers(gsr, orc, offset):
+    """Operands at 2-byte (but not 16-byte) aligned addresses take the
+    element-wise path and give the same results."""
+    M, N, K = 130, 136, 72
+    a, b = W.normal_inputs(M, N, K, seed=offset)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
+    say(f"[gpu] unaligned offset {offset}")
+    abuf = torch.zeros(M * K + 64, dtype=torch.float16, device=DEV)
+    bbuf = torch.zeros(K * N + 64, dtype=torch.float16, device=DEV)
+    cbuf = torch.zeros(M * N + 64, dtype=torch.float16, device=DEV)
+    ad = abuf[offset:offset + M * K].view(M, K)
+    bd = bbuf[offset:offset + K * N].view(K, N)
+    cd = cbuf[offset:offset + M * N].view(M, N)
+    ad.copy_(a.to(DEV))
+    bd.copy_(b.to(DEV))
+    gsr.gemm_scale_relu(ad, bd, 0.5, c=cd)
+    torch.cuda.synchronize()
+    PT.assert_parity(f"unaligned+{offset}", bits(cd.cpu()), ref)
+
+
+@pytest.mark.parametrize("cid", [-1, 0, 5])
+def test_guard_bands_and_full_coverage(gsr, orc, cid):
+    """C sits inside a larger buffer filled with a sentinel: the bands before
+    and after stay untouched and every element of C is written."""
+    M, N, K = 333, 264, 136
+    a, b = W.normal_inputs(M, N, K, seed=21)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 1.0)
+    say(f"[gpu] guard bands config {cid}")
+    guard = 4096
+    # a NaN payload no kernel would produce; filled as int16 so the exact bits survive
+    buf = torch.full((guard + M * N + guard,), 0x7E5A, dtype=torch.int16, device=DEV).view(torch.float16)
+    c = buf[guard:guard + M * N].view(M, N)
+    PT.run_gpu(a, b, 1.0, config_id=cid, c=c)
+    hb = bits(buf.cpu())
+    assert np.all(hb[:guard] == 0x7E5A) and np.all(hb[guard + M * N:] == 0x7E5A)
+    PT.assert_parity(f"guard cfg{cid}", hb[guard:guard + M * N].reshape(M, N), ref)
+
+
+def test_zero_padding_equivalence(gsr):
+    """A ragged problem and its zero-padded, tile-multiple version agree bit
+    for bit on the shared block (adding exact zeros leaves fp32 sums alone)."""
+    M, N, K = 261, 300, 150
+    a, b = W.normal_inputs(M, N, K, seed=4)
+    ap = torch.zeros(512, 512, dtype=torch.float16)
+    bp = torch.zeros(192, 512, dtype=torch.float16)
+    ap[:M, :K] = a
+    bp[:K, :N] = b
+    ap = ap[:, :192].contiguous()
+    for cid in range(gsr.num_configs()):
+        say(f"[gpu] zero padding config {cid}")
+        got = PT.run_gpu(a, b, 0.5, config_id=cid)
+        gotp = PT.run_gpu(ap, bp, 0.5, config_id=cid)
+        PT.assert_bitwise(f"padding cfg{cid}", got, gotp[:M, :N])
+        assert np.all(gotp[M:, :] == 0) and np.all(gotp[:, N:] == 0)
+
+
+def test_nonpositive_results_are_plus_zero(gsr):
+    """An exactly-zero sum times a negative alpha is -0 in fp32; ReLU must
+    still store +0."""
+    say("[gpu] -0 handling")
+    a = torch.zeros((64, 64), dtype=torch.float16, device=DEV)
+    b = torch.ones((64, 64), dtype=torch.float16, device=DEV)
+    c = gsr.gemm_scale_relu(a, b, -0.5)
+    torch.cuda.synchronize()
+    assert not torch.any(torch.signbit(c))
+
+
+def test_alpha_sign_flip(gsr):
+    M, N, K = 512, 640, 384
+    a, b = W.normal_inputs(M, N, K, seed=8)
+    say("[gpu] alpha sign flip")
+    p = PT.run_gpu(a, b, 0.75)
+    n = PT.run_gpu(a, b, -0.75)
+    assert not np.any((p != 0) & (n != 0))
+    assert not np.any(p & 0x8000) and not np.any(n & 0x8000)
+
+
+def test_transpose_invariant(gsr):
+    """(A B)^T = B^T A^T, bit for bit with integer inputs."""
+    M, N, K = 320, 200, 264
+    a, b = W.integer_inputs(M, N, K, seed=9)
+    say("[gpu] transpose")
+    c = PT.run_gpu(a, b, 0.5)
+    ct = PT.run_gpu(b.t().contiguous(), a.t().contiguous(), 0.5)
+    PT.assert_bitwise("transpose", ct, c.T)
+
+
+def test_deterministic(gsr):
+    w = W.WORKLOADS["square_1024"]
+    a, b = W.workload_inputs(w)
+    ad, bd = a.to(DEV), b.to(DEV)
+    say("[gpu] determinism")
+    first = gsr.gemm_scale_relu(ad, bd, w.alpha)
+    for _ in range(20):
+        again = gsr.gemm_scale_relu(ad, bd, w.alpha)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_side_stream(gsr, orc):
+    M, N, K = 256, 512, 320
+    a, b = W.normal_inputs(M, N, K, seed=13)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
+    say("[gpu] side stream")
+    s = torch.cuda.Stream()
+    ad, bd = a.to(DEV), b.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = gsr.gemm_scale_relu(ad, bd, 0.5)
+    s.synchronize()
+    PT.assert_parity("side stream", bits(c.cpu()), ref)
+
+
+def test_graph_capture_replays(gsr, orc):
+    """The launch can be captured into a HIP graph; each replay, with eager
+    work in between, matches the eager result."""
+    M, N, K = 1024, 1024, 1024
+    a, b = W.normal_inputs(M, N, K, seed=17)
+    ad, bd = a.to(DEV), b.to(DEV)
+    say("[gpu] graph capture")
+    eager = gsr.gemm_scale_relu(ad, bd, 0.5)
+    torch.cuda.synchronize()
+    c = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gsr.gemm_scale_relu(ad, bd, 0.5, c=c)  # warm-up outside capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        gsr.gemm_scale_relu(ad, bd, 0.5, c=c)
+    for i in range(4):
+        c.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        _ = (ad.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()

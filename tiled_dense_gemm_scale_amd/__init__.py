@@ -1,0 +1,77 @@
+"""Fused fp16 GEMM + scale + ReLU for AMD Instinct MI355X (gfx950).
+
+    C = ReLU(alpha * A @ B)    A: (M,K) fp16, B: (K,N) fp16, C: (M,N) fp16
+
+fp32 accumulation, scale and ReLU applied to the fp32 sum in registers, one
+fp16 store (PKUHPC scow-tutorial "Tutorial14", section 3 display formula;
+section 2 listing for the types and the epilogue order).
+
+The compute runs in libgsr.so's hand-written HIP kernels; this package only
+marshals torch tensors (device memory and the current stream) into the C ABI
+of include/gsr.h.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _native
+from ._native import GsrError, get_config, num_configs, select_config, status_string, version
+
+__all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "GsrError", "select_config", "get_config",
+           "num_configs", "status_string", "version", "configs"]
+
+
+def _check_operands(a: torch.Tensor, b: torch.Tensor, c: Optional[torch.Tensor]):
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch: A {tuple(a.shape)} @ B {tuple(b.shape)}")
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("A and B must be row-major contiguous")
+    M, K = a.shape
+    N = b.shape[1]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    elif c.dtype != torch.float16 or tuple(c.shape) != (M, N) or not c.is_contiguous() or not c.is_cuda:
+        raise ValueError("C must be a contiguous (M,N) float16 device tensor")
+    return int(M), int(N), int(K), c
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gemm_scale_relu(a: torch.Tensor, b: torch.Tensor, alpha: float,
+                    c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C = ReLU(alpha * a @ b), enqueued on `stream` (default: the current
+    stream of a's device).  Allocates C when `c` is not given, as the
+    tutorial's kernel wrapper does; returns C."""
+    M, N, K, c = _check_operands(a, b, c)
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_relu(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), alpha, s)
+    _native.check(st)
+    return c
+
+
+def gemm_scale_relu_ex(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id: int,
+                       c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """As gemm_scale_relu with a forced tile configuration (-1 = selector)."""
+    M, N, K, c = _check_operands(a, b, c)
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_relu_ex(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), alpha, s,
+                                        config_id)
+    _native.check(st)
+    return c
+
+
+def configs() -> list:
+    """Every compiled tile configuration."""
+    return [get_config(i) for i in range(num_configs())]

@@ -1,0 +1,345 @@
+// gsr_kernels.hpp -- gfx950 kernels for C = ReLU(alpha * A @ B), fp16 in/out,
+// fp32 accumulation (PKUHPC scow-tutorial "Tutorial14", section 3 display
+// formula; section 2's listing: one workgroup per output tile, a pipelined K
+// loop of global->shared copies and tile products, the scale and max(., 0) on
+// the accumulator fragment, one store).
+//
+// The CDNA4 form of that design:
+//  * one workgroup per BM x BN tile of C, launched on a 1-D grid whose ids are
+//    regrouped so that the eight XCDs each get a compact block of tiles
+//    (their L2s are private) and tiles inside a block share A and B panels;
+//  * K is walked in BK = 64 steps through a ring of LDS buffers.  The loads
+//    for step t+1 are issued into registers before the MFMAs of step t, and
+//    written to the other LDS buffer after them, so global latency hides
+//    behind the math and each step needs one barrier;
+//  * loads are raw buffer loads: out-of-range offsets return zero, which is
+//    the ragged-edge rule (missing A/B elements contribute nothing), and
+//    out-of-range buffer stores are dropped (nothing outside C is written);
+//  * B arrives N-contiguous but an MFMA operand wants 8 K-contiguous values
+//    per lane, so each thread loads an 8x8 block of B, transposes it in
+//    registers with byte permutes and writes K-contiguous rows to LDS.  Both
+//    LDS tiles are then [rows][BK] with 16-byte chunks XOR-swizzled by row,
+//    which keeps the 128-bit writes and the 128-bit fragment reads free of
+//    bank conflicts;
+//  * the MFMA runs with B^T as its first operand and A^T as its second, so
+//    the 32x32 accumulator block lands with four consecutive n per lane: the
+//    epilogue scales, clamps at zero, converts with round-to-nearest-even and
+//    stores 8 bytes per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gsr {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Any byte offset at or past a buffer's num_records reads as zero and is not
+// written; every matrix is below 2^31 bytes, so this one always is.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    // flags word: the raw-buffer data format used on gfx9-family parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte chunk c of LDS row r lives at chunk c ^ swz(r) (8 chunks per row).
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r ^ (r >> 3)) & 7u; }
+
+// Eight consecutive fp16 values starting at element offset `elem`; the first
+// `nvalid` of them exist (0..8).  The vector form needs nvalid in {0, 8} and
+// a 16-byte aligned address.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t rs, uint32_t elem, int nvalid)
+{
+    if constexpr (VEC) {
+        const uint32_t off = (nvalid > 0) ? elem * 2u : kOutOfRange;
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t off = (e < nvalid) ? (elem + e) * 2u : kOutOfRange;
+            h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        }
+        u32x4 v;
+        v[0] = h[0] | (h[1] << 16);
+        v[1] = h[2] | (h[3] << 16);
+        v[2] = h[4] | (h[5] << 16);
+        v[3] = h[6] | (h[7] << 16);
+        return v;
+    }
+}
+
+// lo halves of x and y -> one dword (x low), hi halves likewise
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+
+// In: r[i] = 8 fp16 of row i (columns 0..7).  Out: o[j] = 8 fp16 of column j
+// (rows 0..7).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8])
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {      // row pair (2e, 2e+1) -> dword e of every output
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {  // dword d of a row holds columns 2d, 2d+1
+            o[2 * d][e] = pack_lo(r[2 * e][d], r[2 * e + 1][d]);
+            o[2 * d + 1][e] = pack_hi(r[2 * e][d], r[2 * e + 1][d]);
+        }
+    }
+}
+
+struct Problem {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* C;
+    int M, N, K;
+    float alpha;
+    int tiles_m, tiles_n;
+    int group_m;
+    int xcd_remap;
+};
+
+// Workgroup id -> (tile row, tile column).
+__device__ __forceinline__ void tile_of(int pid, int nwg, const Problem& p, int& tm, int& tn)
+{
+    if (p.xcd_remap) {
+        // Workgroups are handed to the 8 XCDs round-robin: give XCD x a
+        // contiguous range of logical ids instead.
+        const int q = nwg >> 3, r = nwg & 7;
+        const int x = pid & 7, idx = pid >> 3;
+        pid = (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+    }
+    const int per_group = p.group_m * p.tiles_n;
+    const int g = pid / per_group;
+    const int first_m = g * p.group_m;
+    const int gs = min(p.tiles_m - first_m, p.group_m);
+    const int within = pid - g * per_group;
+    tm = first_m + within % gs;
+    tn = within / gs;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+struct TileKernel {
+    static constexpr int NT = kWave * WM * WN;  // threads per workgroup
+    static constexpr int CH = BK / 8;           // 16-byte chunks per LDS row
+    static constexpr int WTM = BM / WM;         // wave tile rows (m)
+    static constexpr int WTN = BN / WN;         // wave tile cols (n)
+    static constexpr int TM = WTM / 32;         // 32x32 MFMA blocks per wave, m
+    static constexpr int TN = WTN / 32;         // ... n
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int A_CHUNKS = BM * CH;               // 16-byte chunks of an A tile
+    static constexpr int A_PER = A_CHUNKS / NT;            // per thread
+    static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);   // 8x8 blocks of a B tile
+    static constexpr int B_PER = (B_BLOCKS + NT - 1) / NT; // per thread (last may be partial)
+
+    static_assert(BK == 64, "the LDS swizzle assumes 8 chunks per row");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(A_CHUNKS % NT == 0 && NT % CH == 0, "A tile must split evenly over threads");
+    static_assert(LDS_BYTES <= 163840, "LDS budget of one workgroup on gfx950");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, bool VEC>
+__global__ void __launch_bounds__(kWave * WM * WN)
+gemm_scale_relu_kernel(Problem p)
+{
+    using T = TileKernel<BM, BN, BK, WM, WN, VEC>;
+    constexpr int NT = T::NT, CH = T::CH, TM = T::TM, TN = T::TN;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const uint32_t a_bytes = (uint32_t)p.M * (uint32_t)p.K * 2u;
+    const uint32_t b_bytes = (uint32_t)p.K * (uint32_t)p.N * 2u;
+    const uint32_t c_bytes = (uint32_t)p.M * (uint32_t)p.N * 2u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, b_bytes);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, c_bytes);
+
+    // ---- this thread's share of each global -> LDS copy -------------------
+    // A: chunk ids tid + i*NT; since NT is a multiple of CH the chunk column is
+    // the same for every i.
+    const int a_kc = tid % CH;
+    const int a_r0 = tid / CH;
+    constexpr int A_ROW_STEP = NT / CH;
+    // B: 8x8 block ids tid + i*NT, block (kb, nb) = rows kb*8.., cols nb*8..
+    constexpr int NB8 = BN / 8;
+
+    u32x4 areg[T::A_PER];
+    u32x4 breg[T::B_PER][8];
+
+    auto load_tile = [&](int k0) {
+        {
+            const int kk = k0 + a_kc * 8;
+            const int kval = min(max(p.K - kk, 0), 8);
+#pragma unroll
+            for (int i = 0; i < T::A_PER; ++i) {
+                const int r = a_r0 + i * A_ROW_STEP;
+                const int m = m0 + r;
+                const int nv = (m < p.M) ? kval : 0;
+                areg[i] = load8<VEC>(ra, (uint32_t)m * (uint32_t)p.K + (uint32_t)kk, nv);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_PER; ++i) {
+            const int blk = tid + i * NT;
+            if (T::B_BLOCKS % NT == 0 || blk < T::B_BLOCKS) {
+                const int kb = blk / NB8, nb = blk % NB8;
+                const int n = n0 + nb * 8;
+                const int nval = min(max(p.N - n, 0), 8);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int k = k0 + kb * 8 + j;
+                    const int nv = (k < p.K) ? nval : 0;
+                    breg[i][j] = load8<VEC>(rb, (uint32_t)k * (uint32_t)p.N + (uint32_t)n, nv);
+                }
+            }
+        }
+    };
+
+    auto store_tile = [&](int stage) {
+        uint8_t* As = smem + stage * T::STAGE_BYTES;
+        uint8_t* Bs = As + T::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::A_PER; ++i) {
+            const uint32_t r = a_r0 + i * A_ROW_STEP;
+            *(u32x4*)(As + r * (BK * 2) + ((a_kc ^ swz(r)) << 4)) = areg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_PER; ++i) {
+            const int blk = tid + i * NT;
+            if (T::B_BLOCKS % NT == 0 || blk < T::B_BLOCKS) {
+                const uint32_t kb = blk / NB8, nb = blk % NB8;
+                u32x4 col[8];
+                transpose8x8(breg[i], col);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t r = nb * 8 + j;
+                    *(u32x4*)(Bs + r * (BK * 2) + ((kb ^ swz(r)) << 4)) = col[j];
+                }
+            }
+        }
+    };
+
+    // ---- fragment addresses -----------------------------------------------
+    // MFMA 32x32x16: lane l supplies row (l % 32) of its 32-row operand block
+    // and the 8 consecutive k of chunk (2*s + l/32) in k-substep s.
+    const uint32_t frow = lane & 31;
+    const uint32_t fhi = lane >> 5;
+    uint32_t xoff[TN], xsw[TN], yoff[TM], ysw[TM];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const uint32_t r = wn * T::WTN + t * 32 + frow;
+        xoff[t] = T::A_BYTES + r * (BK * 2);
+        xsw[t] = swz(r);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const uint32_t r = wm * T::WTM + t * 32 + frow;
+        yoff[t] = r * (BK * 2);
+        ysw[t] = swz(r);
+    }
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    const int ksteps = (p.K + BK - 1) / BK;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ksteps; ++t) {
+        const int cur = t & 1;
+        const bool more = (t + 1) < ksteps;
+        if (more) load_tile((t + 1) * BK);
+
+        const uint8_t* base = smem + cur * T::STAGE_BYTES;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const uint32_t c = 2 * s + fhi;
+            half8 xf[TN], yf[TM];
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+                xf[a] = __builtin_bit_cast(half8, *(const u32x4*)(base + xoff[a] + ((c ^ xsw[a]) << 4)));
+#pragma unroll
+            for (int b = 0; b < TM; ++b)
+                yf[b] = __builtin_bit_cast(half8, *(const u32x4*)(base + yoff[b] + ((c ^ ysw[b]) << 4)));
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int b = 0; b < TM; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[a], yf[b], acc[a][b], 0, 0, 0);
+        }
+
+        if (more) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: scale, clamp at zero, narrow, store ---------------------
+    // Accumulator block (a, b): lane l holds m = l % 32 and, in register
+    // 4g + i, n = 8g + 4*(l/32) + i.
+    const float alpha = p.alpha;
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+            const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
+                half4 h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = acc[a][b][4 * g + i] * alpha;
+                    h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                }
+                const u32x2 w = __builtin_bit_cast(u32x2, h);
+                const uint32_t elem = (uint32_t)m * (uint32_t)p.N + (uint32_t)n;
+                if constexpr (VEC) {
+                    const uint32_t off = (m < p.M && n < p.N) ? elem * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t off = (m < p.M && n + i < p.N) ? (elem + i) * 2u : kOutOfRange;
+                        const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
+                        __builtin_amdgcn_raw_buffer_store_b16(hv, rc, off, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// K == 0: every output is the empty sum, i.e. +0.
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint16_t* C, uint32_t count)
+{
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, count * 2u);
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < count; i += gridDim.x * 256u)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rc, i * 2u, 0, 0);
+}
+
+}  // namespace gsr
