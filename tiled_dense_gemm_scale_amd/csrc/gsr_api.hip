@@ -9,6 +9,9 @@
 
 #include "gsr.h"
 #include "gsr_kernels.hpp"
+#include "gsr_pipeline.hpp"
+#include "gsr_bt.hpp"
+#include "gsr_interleave.hpp"
 
 namespace {
 
@@ -17,51 +20,127 @@ using gsr::Problem;
 typedef hipError_t (*launch_fn)(const Problem&, int grid, hipStream_t);
 
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
-hipError_t launch(const Problem& p, int grid, hipStream_t s)
+hipError_t launch_staged(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL((gsr::gemm_scale_relu_kernel<BM, BN, BK, WM, WN, VEC>), dim3(grid),
                        dim3(gsr::kWave * WM * WN), 0, s, p);
     return hipGetLastError();
 }
 
+template <int BM, int BN, int BK, int WM, int WN, int S>
+hipError_t launch_pipe(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gsr::gemm_scale_relu_pipe_kernel<BM, BN, BK, WM, WN, S>), dim3(grid),
+                       dim3(gsr::kWave * WM * WN), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gsr::gemm_scale_relu_bt_kernel<BM, BN, WM, WN>), dim3(grid), dim3(gsr::kWave * WM * WN), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), 0, s, p);
+    return hipGetLastError();
+}
+
 struct Entry {
     gsr_config cfg;
-    launch_fn vec;   // 128-bit path
-    launch_fn elem;  // element-wise path
+    launch_fn vec;   // 128-bit path (16-byte aligned A/B, K and N multiples of 8)
+    launch_fn elem;  // element-wise path, any 2-byte aligned layout
 };
 
-#define GSR_ENTRY(ID, BM, BN, BK, WM, WN, GROUP)                                                      \
+// Pipelined kernel: LDS ring of S stages filled by direct-to-LDS copies.  The
+// element-wise path of the same tile is the register-staged kernel.
+#define GSR_PIPE(ID, BM, BN, BK, WM, WN, S, GROUP)                                                    \
     Entry                                                                                             \
     {                                                                                                 \
-        {ID, BM, BN, BK, WM, WN, 2, GROUP, 1, gsr::TileKernel<BM, BN, BK, WM, WN, true>::LDS_BYTES}, \
-            launch<BM, BN, BK, WM, WN, true>, launch<BM, BN, BK, WM, WN, false>                      \
+        {ID, BM, BN, BK, WM, WN, S, GROUP, 1, gsr::PipeCfg<BM, BN, BK, WM, WN, S>::LDS_BYTES},       \
+            launch_pipe<BM, BN, BK, WM, WN, S>, launch_staged<BM, BN, 64, WM, WN, false>              \
+    }
+// Register-staged kernel (two LDS buffers, global loads one step ahead in
+// registers, B transposed in registers).  stages = 0 marks this kind.
+#define GSR_STAGED(ID, BM, BN, WM, WN, GROUP)                                                         \
+    Entry                                                                                             \
+    {                                                                                                 \
+        {ID, BM, BN, 64, WM, WN, 0, GROUP, 1, gsr::TileKernel<BM, BN, 64, WM, WN, true>::LDS_BYTES}, \
+            launch_staged<BM, BN, 64, WM, WN, true>, launch_staged<BM, BN, 64, WM, WN, false>        \
+    }
+
+// A by direct-to-LDS copies, B transposed in registers: every operand read is
+// 128 bits.  stages = 1 marks this kind (two LDS buffers for each operand).
+#define GSR_BT(ID, BM, BN, WM, WN, GROUP)                                                             \
+    Entry                                                                                             \
+    {                                                                                                 \
+        {ID, BM, BN, 64, WM, WN, 1, GROUP, 1, gsr::BtCfg<BM, BN, WM, WN>::LDS_BYTES},                 \
+            launch_bt<BM, BN, WM, WN>, launch_staged<BM, BN, 64, WM, WN, false>                       \
     }
 
 // The compiled tile table.  Tile choice per shape class is made by select().
 const Entry kTable[] = {
-    GSR_ENTRY(0, 256, 256, 64, 2, 4, 4),  // large: 8 waves of 128x64
-    GSR_ENTRY(1, 256, 128, 64, 2, 2, 4),  // 4 waves of 128x64
-    GSR_ENTRY(2, 128, 256, 64, 2, 2, 4),  // 4 waves of 64x128
-    GSR_ENTRY(3, 128, 128, 64, 2, 2, 4),  // 4 waves of 64x64
-    GSR_ENTRY(4, 128, 64, 64, 2, 2, 4),   // 4 waves of 64x32
-    GSR_ENTRY(5, 64, 64, 64, 2, 2, 4),    // small: 4 waves of 32x32
+    GSR_PIPE(0, 256, 256, 64, 2, 4, 2, 4),   // 8 waves of 128x64, 2 x 64 KiB
+    GSR_PIPE(1, 256, 256, 32, 2, 4, 4, 4),   // 8 waves of 128x64, 4 x 32 KiB
+    GSR_PIPE(2, 256, 256, 32, 2, 4, 3, 4),   // 8 waves of 128x64, 3 x 32 KiB
+    GSR_PIPE(3, 256, 256, 64, 2, 2, 2, 4),   // 4 waves of 128x128
+    GSR_PIPE(4, 256, 256, 32, 2, 2, 4, 4),   // 4 waves of 128x128
+    GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
+    GSR_PIPE(6, 128, 256, 64, 2, 2, 3, 4),   // 4 waves of 64x128
+    GSR_PIPE(7, 128, 128, 64, 2, 2, 4, 4),   // 4 waves of 64x64, 4 x 32 KiB
+    GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
+    GSR_PIPE(9, 64, 64, 64, 2, 2, 8, 4),     // 4 waves of 32x32, 8 x 16 KiB
+    GSR_PIPE(10, 64, 128, 64, 2, 2, 6, 4),   // 4 waves of 32x64
+    GSR_STAGED(11, 256, 256, 2, 4, 4),
+    GSR_STAGED(12, 128, 128, 2, 2, 4),
+    GSR_STAGED(13, 64, 64, 2, 2, 4),
+    GSR_BT(14, 256, 256, 2, 2, 4),           // 4 waves of 128x128
+    // explicit interleave, 4 waves of 128x128; stages = 1 as for GSR_BT
+    Entry{{15, 256, 256, 64, 2, 2, 1, 4, 1, gsr::IlvCfg::LDS_BYTES}, launch_ilv, launch_staged<256, 256, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape classes: enough workgroups to cover the 256 CUs with the largest
-// tile that still does so; otherwise fall back to smaller tiles.
-int select(int64_t M, int64_t N, int64_t /*K*/)
+// Tile selection.  Each candidate's cost is the number of waves of workgroups
+// it needs on 256 CUs times the work of one tile, divided by the rate one CU
+// sustains on that tile when every CU is busy (measured on MI355X at
+// 16384^3).  Large tiles win when there are enough of them to fill the chip;
+// small shapes fall back to small tiles that spread over more CUs.
+struct Candidate {
+    int id;
+    double tflops_per_cu;
+};
+const Candidate kCandidates[] = {
+    {15, 4.69},  // 256x256, explicit interleave
+    {0, 4.35},   // 256x256, 8 waves, transposing LDS reads
+    {5, 3.52},   // 256x128
+    {6, 3.52},   // 128x256
+    {7, 2.88},   // 128x128
+    {8, 2.08},   // 128x64
+    {10, 2.09},  // 64x128
+    {9, 1.80},   // 64x64
+};
+
+int select(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t cus = 256;
-    const int order[] = {0, 1, 2, 3, 4, 5};
-    for (int id : order) {
-        const gsr_config& c = kTable[id].cfg;
-        const int64_t wgs = cdiv(M, c.block_m) * cdiv(N, c.block_n);
-        if (wgs >= cus) return id;
+    const double cus = 256.0;
+    int best = 9;
+    double best_t = 1e300;
+    for (const Candidate& c : kCandidates) {
+        const gsr_config& g = kTable[c.id].cfg;
+        const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
+        const double waves = std::ceil(wgs / cus);
+        const double t = waves * 2.0 * g.block_m * g.block_n * (double)(K > 0 ? K : 1) / c.tflops_per_cu;
+        if (t < best_t) {
+            best_t = t;
+            best = c.id;
+        }
     }
-    return 5;
+    return best;
 }
 
 struct DeviceInfo {

@@ -319,12 +319,12 @@ gemm_scale_relu_kernel(Problem p)
                 const u32x2 w = __builtin_bit_cast(u32x2, h);
                 const uint32_t elem = (uint32_t)m * (uint32_t)p.N + (uint32_t)n;
                 if constexpr (VEC) {
-                    const uint32_t off = (m < p.M && n < p.N) ? elem * 2u : kOutOfRange;
+                    const uint32_t off = ((m < p.M) & (n < p.N)) ? elem * 2u : kOutOfRange;
                     __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t off = (m < p.M && n + i < p.N) ? (elem + i) * 2u : kOutOfRange;
+                        const uint32_t off = ((m < p.M) & (n + i < p.N)) ? (elem + i) * 2u : kOutOfRange;
                         const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
                         __builtin_amdgcn_raw_buffer_store_b16(hv, rc, off, 0, 0);
                     }
