@@ -43,7 +43,7 @@ def test_config_table(native):
     for i in range(n):
         c = native.get_config(i)
         assert c["id"] == i
-        assert c["block_k"] in (32, 64)
+        assert c["block_k"] in (32, 64, 128)
         assert c["block_m"] % (32 * c["waves_m"]) == 0 and c["block_n"] % (32 * c["waves_n"]) == 0
         # stages == 0: register-staged kernel with two LDS buffers;
         # stages == 1: A copied to LDS, B transposed through registers, two

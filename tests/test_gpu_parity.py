@@ -189,7 +189,8 @@ def test_guard_bands_and_full_coverage(gsr, orc, cid):
 def test_zero_padding_equivalence(gsr):
     """A ragged problem and its zero-padded, tile-multiple version agree bit
     for bit on the shared block (adding exact zeros leaves fp32 sums alone)."""
-    M, N, K = 261, 300, 150
+    # K and N multiples of 8 so both problems take the same (128-bit) path
+    M, N, K = 261, 296, 152
     a, b = W.normal_inputs(M, N, K, seed=4)
     ap = torch.zeros(512, 512, dtype=torch.float16)
     bp = torch.zeros(192, 512, dtype=torch.float16)

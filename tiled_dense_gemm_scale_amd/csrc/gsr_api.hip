@@ -12,6 +12,7 @@
 #include "gsr_pipeline.hpp"
 #include "gsr_bt.hpp"
 #include "gsr_interleave.hpp"
+#include "gsr_ksplit.hpp"
 
 namespace {
 
@@ -49,6 +50,13 @@ hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int BM, int BN, int S>
+hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((gsr::gemm_scale_relu_ksplit_kernel<BM, BN, S>), dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 struct Entry {
     gsr_config cfg;
     launch_fn vec;   // 128-bit path (16-byte aligned A/B, K and N multiples of 8)
@@ -81,6 +89,15 @@ struct Entry {
             launch_bt<BM, BN, WM, WN>, launch_staged<BM, BN, 64, WM, WN, false>                       \
     }
 
+// Four waves splitting K inside the workgroup (block_k = 128 per step, waves
+// 1 x 1 over the output tile), LDS ring of S stages.
+#define GSR_KSPLIT(ID, BM, BN, S, GROUP)                                                              \
+    Entry                                                                                             \
+    {                                                                                                 \
+        {ID, BM, BN, 128, 1, 1, S, GROUP, 1, gsr::KsCfg<BM, BN, S>::LDS_BYTES},                       \
+            launch_ksplit<BM, BN, S>, launch_staged<64, 64, 64, 2, 2, false>                          \
+    }
+
 // The compiled tile table.  Tile choice per shape class is made by select().
 const Entry kTable[] = {
     GSR_PIPE(0, 256, 256, 64, 2, 4, 2, 4),   // 8 waves of 128x64, 2 x 64 KiB
@@ -100,6 +117,10 @@ const Entry kTable[] = {
     GSR_BT(14, 256, 256, 2, 2, 4),           // 4 waves of 128x128
     // explicit interleave, 4 waves of 128x128; stages = 1 as for GSR_BT
     Entry{{15, 256, 256, 64, 2, 2, 1, 4, 1, gsr::IlvCfg::LDS_BYTES}, launch_ilv, launch_staged<256, 256, 64, 2, 2, false>},
+    GSR_KSPLIT(16, 64, 64, 4, 4),            // 4 waves split K, whole 64x64 tile each
+    GSR_KSPLIT(17, 64, 32, 6, 4),
+    GSR_KSPLIT(18, 32, 64, 6, 4),
+    GSR_KSPLIT(19, 64, 64, 5, 4),            // one more stage in flight (160 KiB)
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -108,8 +129,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  Each candidate's cost is the number of waves of workgroups
 // it needs on 256 CUs times the work of one tile, divided by the rate one CU
 // sustains on that tile when every CU is busy (measured on MI355X at
-// 16384^3).  Large tiles win when there are enough of them to fill the chip;
-// small shapes fall back to small tiles that spread over more CUs.
+// 16384^3, or at the long-K end of a K sweep for the small tiles).  Large
+// tiles win when there are enough of them to fill the chip; small shapes fall
+// back to small tiles that spread over more CUs.
 struct Candidate {
     int id;
     double tflops_per_cu;
@@ -122,7 +144,9 @@ const Candidate kCandidates[] = {
     {7, 2.88},   // 128x128
     {8, 2.08},   // 128x64
     {10, 2.09},  // 64x128
+    {16, 2.00},  // 64x64, four waves splitting K
     {9, 1.80},   // 64x64
+    {18, 1.05},  // 32x64, four waves splitting K
 };
 
 int select(int64_t M, int64_t N, int64_t K)

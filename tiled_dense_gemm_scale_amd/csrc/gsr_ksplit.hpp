@@ -1,0 +1,265 @@
+// gsr_ksplit.hpp -- small-tile 128-bit path of C = ReLU(alpha * A @ B) for
+// shapes with few output tiles (e.g. 1024^3 gives 256 tiles of 64x64, one per
+// CU) and for skinny shapes.
+//
+// With a 64x64 tile split over four waves by output, each wave gets a single
+// 32x32 MFMA per 16-k substep, and every K-step becomes a chain of LDS
+// latency, one MFMA and a barrier.  Here the four waves split K instead: each
+// K-step covers BK = 128 (eight 16-k substeps) and wave w computes substeps w
+// and w+4 for the whole BM x BN tile, so a wave issues 8..16 MFMAs per step
+// and the operand bytes each wave reads per MFMA halve.
+//  * A and B are copied global -> LDS by the buffer unit (buffer_load ... lds)
+//    into a ring of STAGES buffers kept STAGES-1 steps ahead; out-of-range
+//    chunks read as zero (ragged M, N, K).
+//  * A lands as [BM][128] rows (16-byte chunks XOR-swizzled by row), read with
+//    128-bit LDS reads; B lands as [128][BN] rows and is read with the gfx950
+//    transpose read, which hands each lane four K-consecutive values of one
+//    column.
+//  * The operand reads of step t are issued right after the barrier that
+//    publishes step t, and the MFMAs of step t-1 run behind them.
+//  * At the end the four partial tiles are summed through LDS in the MFMA
+//    lane layout (each 1 KiB write and read is contiguous), and each wave
+//    stores a quarter of the tile: scale, clamp at zero, round to fp16.
+#pragma once
+
+#include "gsr_pipeline.hpp"
+
+namespace gsr {
+
+template <int BM, int BN, int STAGES>
+struct KsCfg {
+    static constexpr int BK = 128, NW = 4, NT = kWave * NW;
+    static constexpr int CHA = BK / 8;   // 16 chunks per A row (256 bytes)
+    static constexpr int CHN = BN / 8;   // chunks per B row
+    static constexpr int TM = BM / 32, TN = BN / 32;
+    static constexpr int NB = TM * TN;  // accumulator blocks per wave
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int RED_BYTES = NW * NB * 4 * 1024;  // partial tiles for the reduction
+    static constexpr int LDS_BYTES = (STAGES * STAGE_BYTES > RED_BYTES) ? STAGES * STAGE_BYTES : RED_BYTES;
+    static constexpr int A_PER = A_BYTES / 1024 / NW;  // copies per wave per step
+    static constexpr int B_PER = B_BYTES / 1024 / NW;
+    static constexpr int LOADS = A_PER + B_PER;
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && CHN >= 4, "tile");
+    static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "copies split over waves");
+    static_assert((NB * 4) % NW == 0, "reduction units split over waves");
+    static_assert(STAGES >= 2 && LDS_BYTES <= 163840, "LDS");
+};
+
+// 16-chunk (256-byte) A rows: chunk c of row r sits at c ^ f(r); any 16
+// consecutive rows read at one logical chunk hit 16 distinct positions.
+__device__ __forceinline__ uint32_t swz_a16(uint32_t r) { return (r ^ (r >> 4)) & 15u; }
+
+template <int BM, int BN, int STAGES>
+__global__ void __launch_bounds__(256)
+gemm_scale_relu_ksplit_kernel(Problem p)
+{
+    using T = KsCfg<BM, BN, STAGES>;
+    constexpr int BK = T::BK, NW = T::NW, CHA = T::CHA, CHN = T::CHN, TM = T::TM, TN = T::TN, NB = T::NB;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const i32x4 ra = raw_rsrc(p.A, (uint32_t)p.M * (uint32_t)p.K * 2u);
+    const i32x4 rb = raw_rsrc(p.B, (uint32_t)p.K * (uint32_t)p.N * 2u);
+    const uint32_t lds0 = lds_address(smem);
+
+    // ---- copy plan ------------------------------------------------------------
+    uint32_t a_off[T::A_PER];
+    int a_k[T::A_PER];
+    bool a_ok[T::A_PER];
+#pragma unroll
+    for (int i = 0; i < T::A_PER; ++i) {
+        const int P = 64 * (wave + i * NW) + lane;
+        const int r = P / CHA;
+        const int c = (P % CHA) ^ (int)swz_a16((uint32_t)r);
+        const int m = m0 + r;
+        a_ok[i] = m < p.M;
+        a_k[i] = 8 * c;
+        a_off[i] = ((uint32_t)m * (uint32_t)p.K + (uint32_t)(8 * c)) * 2u;
+    }
+    uint32_t b_off[T::B_PER];
+    int b_k[T::B_PER];
+    bool b_ok[T::B_PER];
+#pragma unroll
+    for (int i = 0; i < T::B_PER; ++i) {
+        const int P = 64 * (wave + i * NW) + lane;
+        const int k = P / CHN;
+        const int c = (P % CHN) ^ (int)swz_b<CHN>((uint32_t)k);
+        const int n = n0 + 8 * c;
+        b_ok[i] = n < p.N;
+        b_k[i] = k;
+        b_off[i] = ((uint32_t)k * (uint32_t)p.N + (uint32_t)n) * 2u;
+    }
+    auto issue = [&](int stage, int k0) {
+        const uint32_t As = lds0 + stage * T::STAGE_BYTES;
+        const uint32_t Bs = As + T::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::A_PER; ++i) {
+            const bool ok = a_ok[i] & (k0 + a_k[i] < p.K);
+            copy16_to_lds(ra, ok ? a_off[i] + (uint32_t)k0 * 2u : kOutOfRange, As + (wave + i * NW) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_PER; ++i) {
+            const bool ok = b_ok[i] & (k0 + b_k[i] < p.K);
+            copy16_to_lds(rb, ok ? b_off[i] + (uint32_t)k0 * (uint32_t)p.N * 2u : kOutOfRange, Bs + (wave + i * NW) * 1024);
+        }
+    };
+
+    // ---- operand reads: substeps ks = wave and wave + 4 of each step ---------
+    const uint32_t frow = lane & 31, fhi = lane >> 5;
+    uint32_t y_off[2][TM];  // A rows
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+            const uint32_t r = b * 32 + frow;
+            const uint32_t c = 2u * (uint32_t)(wave + 4 * h) + fhi;
+            y_off[h][b] = r * (BK * 2) + ((c ^ swz_a16(r)) << 4);
+        }
+    // transpose reads of B: 16-lane group G, i = l%16, e = i/4, q = i%4
+    const uint32_t G = lane >> 4, li = lane & 15, e4 = li >> 2, q4 = li & 3;
+    uint32_t x_off[2][2][TN];  // [substep half][read 0/1][n block]
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+                const uint32_t k = 16u * (uint32_t)(wave + 4 * h) + 8u * (G >> 1) + 4u * rd + e4;
+                const uint32_t chunk = (uint32_t)(a * 32 + 16 * (G & 1)) / 8 + (q4 >> 1);
+                x_off[h][rd][a] = (uint32_t)T::A_BYTES + k * (BN * 2) + ((chunk ^ swz_b<CHN>(k)) << 4) + (q4 & 1) * 8;
+            }
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    // Two operand sets: the reads of step t fill set t & 1 while the MFMAs of
+    // step t-1 use the other.  Both start as zeros so no path reads an
+    // unwritten register.
+    half8 xs0[2][TN], ys0[2][TM], xs1[2][TN], ys1[2][TM];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a) xs0[h][a] = xs1[h][a] = (half8)(_Float16)0.0f;
+#pragma unroll
+        for (int b = 0; b < TM; ++b) ys0[h][b] = ys1[h][b] = (half8)(_Float16)0.0f;
+    }
+    auto read_step = [&](int stage, half8 (&xs)[2][TN], half8 (&ys)[2][TM]) {
+        const uint8_t* base = smem + stage * T::STAGE_BYTES;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int b = 0; b < TM; ++b) ys[h][b] = __builtin_bit_cast(half8, *(const u32x4*)(base + y_off[h][b]));
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][0][a]));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][1][a]));
+                xs[h][a] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
+    };
+    auto mma_step = [&](const half8 (&xs)[2][TN], const half8 (&ys)[2][TM]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int b = 0; b < TM; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xs[h][a], ys[h][b], acc[a][b], 0, 0, 0);
+    };
+    // iteration t: wait for step t's copies, publish them, refill the buffer
+    // step t-1 used, read step t, multiply step t-1
+    auto sync_and_refill = [&](int t, int ksteps) {
+        const int ahead = min(STAGES - 2, ksteps - 1 - t);
+        if (ahead == STAGES - 2) wait_vmcnt<T::LOADS * (STAGES - 2)>();
+        else wait_vmcnt_dyn(T::LOADS * ahead);
+        lds_barrier();
+        if (t + STAGES - 1 < ksteps) issue((t + STAGES - 1) % STAGES, (t + STAGES - 1) * BK);
+    };
+
+    const int ksteps = (p.K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < ksteps) issue(s, s * BK);
+
+    int t = 0;
+    for (; t + 1 < ksteps; t += 2) {
+        sync_and_refill(t, ksteps);
+        read_step(t % STAGES, xs0, ys0);
+        if (t > 0) mma_step(xs1, ys1);
+        sync_and_refill(t + 1, ksteps);
+        read_step((t + 1) % STAGES, xs1, ys1);
+        mma_step(xs0, ys0);
+    }
+    if (t < ksteps) {  // odd step count: one more even step
+        sync_and_refill(t, ksteps);
+        read_step(t % STAGES, xs0, ys0);
+        if (t > 0) mma_step(xs1, ys1);
+        mma_step(xs0, ys0);
+    } else if (ksteps > 0) {
+        mma_step(xs1, ys1);
+    }
+
+    // ---- sum the four partial tiles through LDS ---------------------------------
+    wait_vmcnt<0>();
+    lds_barrier();  // every wave is done with the operand buffers
+    // slot (w, blk, g): 64 lanes x 16 bytes, lane-contiguous
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int slot = (wave * NB + a * TM + b) * 4 + g;
+                const f32x16 av = acc[a][b];
+                f32x4 v;
+                if (g == 0) v = __builtin_shufflevector(av, av, 0, 1, 2, 3);
+                else if (g == 1) v = __builtin_shufflevector(av, av, 4, 5, 6, 7);
+                else if (g == 2) v = __builtin_shufflevector(av, av, 8, 9, 10, 11);
+                else v = __builtin_shufflevector(av, av, 12, 13, 14, 15);
+                *(f32x4*)(smem + slot * 1024 + lane * 16) = v;
+            }
+    lds_barrier();
+
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
+    const float alpha = p.alpha;
+    // unit u = blk*4 + g goes to wave u % 4
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int u = j * NW + wave;
+        const int blk = u >> 2, g = u & 3;
+        const int a = blk / TM, b = blk % TM;
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const f32x4 v = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] += v[i];
+        }
+        const int m = m0 + b * 32 + (int)frow;
+        const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = s[i] * alpha;
+            hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+        }
+        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);
+    }
+}
+
+}  // namespace gsr
