@@ -283,29 +283,52 @@ gemm_scale_relu_ilv_kernel(Problem p)
         step(std::integral_constant<int, 0>{}, t);
         step(std::integral_constant<int, 1>{}, t + 1);
     }
-    wait_vmcnt<0>();  // no copy may land in LDS after this workgroup is gone
+    // Drain every load before the epilogue: no copy may land in LDS after the
+    // workgroup is gone, and tying the B registers keeps the compiler from
+    // reusing them while the last (dead) loads into them are in flight.
+    wait_vmcnt_b<0>(breg);
 
     // ---- epilogue ------------------------------------------------------------
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
+    // Scale, ReLU and round in registers, then pass the wave's 128x128 fp16
+    // sub-tile through its own 32 KB of LDS so that the global stores write
+    // whole 256-byte row segments (16 lanes per row) instead of 16 bytes in
+    // each of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at
+    // physical chunk c ^ (r % 16).
+    static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
+    lds_barrier();  // every wave is past its last operand read
     const float alpha = p.alpha;
+    uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
 #pragma unroll
         for (int b = 0; b < TM; ++b) {
-            const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+            const uint32_t r = (uint32_t)b * 32u + frow;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
                 half4 h;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float v = acc[a][b][4 * g + i] * alpha;
                     h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
                 }
-                const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
+                const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
+                *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
             }
         }
+    }
+    // The reads below take what other lanes of this wave wrote: LDS keeps a
+    // wave's accesses in order, so only the compiler must not move them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
+    const uint32_t sc = (uint32_t)lane & 15u;
+    const int n = n0 + wn * T::WTN + 8 * (int)sc;
+#pragma unroll
+    for (int j = 0; j < T::WTM / 4; ++j) {
+        const uint32_t r = 4u * (uint32_t)j + ((uint32_t)lane >> 4);
+        const u32x4 v = *(const u32x4*)(ep + r * 256u + ((sc ^ (r & 15u)) << 4));
+        const int m = m0 + wm * T::WTM + (int)r;
+        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
     }
 }
 
