@@ -59,6 +59,56 @@ def load_traffic(workload: str, flops: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def device_info(index: int) -> dict:
+    """CU count and maximum engine clock as the HIP runtime reports them."""
+    import ctypes
+    info = {}
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            hip = ctypes.CDLL(name)
+            break
+        except OSError:
+            hip = None
+    if hip is None:
+        return info
+    for key, attr in (("clock_khz", 5), ("cus", 63)):  # hipDeviceAttributeClockRate, ...MultiprocessorCount
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, index) == 0:
+            info[key] = v.value
+    return info
+
+
+def time_graph(graph, stream, steps: int, repeats: int):
+    """Per-call milliseconds of `repeats` replays of a graph of `steps` calls,
+    each bracketed by events on the launch stream."""
+    import torch
+    out = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def capture(fn, stream, steps: int):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()  # one untimed replay
+    torch.cuda.synchronize()
+    return g
+
+
 def cpu_baseline(w, a, b, target_s: float):
     """The oracle, as it is, on a bounded sample of the same workload: the
     first R rows of A against all of B, R sized for about `target_s` seconds."""
@@ -100,6 +150,12 @@ def main(argv=None) -> int:
     ap.add_argument("--config-id", type=int, default=-1, help="force a tile configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="extra replays of the timed graph for median/min (graph launch only)")
+    ap.add_argument("--no-context", action="store_true", help="skip the dispatch-floor measurement")
+    ap.add_argument("--zero-input", action="store_true",
+                    help="also time the same kernel on all-zero inputs (runs the timed kernel again, "
+                         "so leave it off when profiling per-kernel averages)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -123,7 +179,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
-    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    dinfo = device_info(torch.cuda.current_device())
+    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} {dinfo}")
     log(f"[bench] workload {w.name}: {w.note}")
 
     a_cpu, b_cpu = W.workload_inputs(w)
@@ -145,13 +202,7 @@ def main(argv=None) -> int:
 
     graph = None
     if args.launch == "graph":
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for _ in range(args.steps):
-                step()
-        torch.cuda.synchronize()
-        graph.replay()  # one untimed replay
-        torch.cuda.synchronize()
+        graph = capture(step, stream, args.steps)
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -172,6 +223,39 @@ def main(argv=None) -> int:
     log(f"[bench] {args.steps} steps in {elapsed_ms:.3f} ms -> {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_FP16_TFLOPS:.1f}% of {PEAK_FP16_TFLOPS})")
 
+    # Context, outside the timed region: the spread of further replays, the
+    # dispatch floor (the same number of launches of the library's smallest
+    # kernel: K = 0 on a 1x8 output) and, on request, the same kernel on
+    # all-zero inputs (identical instruction stream; the engine clock is
+    # power-limited and depends on the data, so this separates the schedule
+    # from the clock).
+    context = {}
+    if graph is not None and args.repeats > 0:
+        reps = sorted(time_graph(graph, stream, args.steps, args.repeats))
+        context["repeat_ms_per_step"] = {"median": round(reps[len(reps) // 2], 6), "min": round(reps[0], 6),
+                                         "max": round(reps[-1], 6), "n": len(reps)}
+        log(f"[bench] repeats: {context['repeat_ms_per_step']}")
+    if graph is not None and not args.no_context:
+        a0 = torch.empty((1, 0), dtype=torch.float16, device=dev)
+        b0 = torch.empty((0, 8), dtype=torch.float16, device=dev)
+        c0 = torch.empty((1, 8), dtype=torch.float16, device=dev)
+        g0 = capture(lambda: gsr.gemm_scale_relu(a0, b0, 1.0, c=c0, stream=stream), stream, args.steps)
+        floor = min(time_graph(g0, stream, args.steps, 3))
+        context["dispatch_floor_us"] = round(floor * 1e3, 3)
+        del g0
+        log(f"[bench] dispatch floor {context['dispatch_floor_us']} us/launch")
+    if graph is not None and args.zero_input:
+        za = torch.zeros_like(a)
+        zb = torch.zeros_like(b)
+        zc = torch.empty_like(c)
+        gz = capture(lambda: gsr.gemm_scale_relu_ex(za, zb, w.alpha, args.config_id, c=zc, stream=stream),
+                     stream, args.steps)
+        zms = min(time_graph(gz, stream, args.steps, 1))
+        context["zero_input_tflops"] = round(w.flops / (zms * 1e-3) / 1e12, 3)
+        del gz, za, zb, zc
+        torch.cuda.empty_cache()
+        log(f"[bench] zero inputs {context['zero_input_tflops']} TFLOP/s")
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 1024 * 1024 // 2
         src = torch.ones(n, dtype=torch.float16, device=dev)
@@ -182,12 +266,19 @@ def main(argv=None) -> int:
         log(f"[bench] copy calibration: {n * 2} bytes read, {n * 2} bytes written")
 
     traffic = load_traffic(w.name, w.flops)
+    # The bound follows the workload's arithmetic intensity against the ridge
+    # point of the two published peaks (2516.6 TFLOP/s / 8 TB/s = 315 FLOP/B).
+    ridge = PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if w.flops / w.algorithmic_bytes >= ridge:
+        achieved, peak, unit, bound = tflops, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = w.algorithmic_bytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     roofline = {
-        "bound": "mfma",
-        "achieved": round(tflops, 3),
-        "peak": PEAK_FP16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "bound": bound,
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4),
         "traffic": traffic,
     }
     cpu = None
@@ -217,6 +308,8 @@ def main(argv=None) -> int:
             "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n")},
             "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
+            "device": {"cus": dinfo.get("cus"), "max_clock_mhz": (dinfo["clock_khz"] / 1000.0) if "clock_khz" in dinfo else None},
+            **context,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -8,16 +8,18 @@
 // (an MFMA plus its companions) at a time, with a scheduling barrier between
 // units so the compiler keeps that order.
 //
-// Per K-step (BK = 64, four 16-k substeps of 16 MFMAs each), units carry:
-//   substep 0: the next substep's operand reads alternating with the A copies
-//              of step t+1 (buffer_load ... lds), then the byte-permute
-//              transpose of the B block of step t+1 (loaded during step t-1);
+// Per K-step t (BK = 64, four 16-k substeps of 16 MFMAs each), units carry:
+//   substep 0: the next substep's operand reads, then the byte-permute
+//              transpose of the B block of step t+1;
 //   substep 1: the next substep's operand reads alternating with the
-//              transposed B writes;
-//   substep 2: the next substep's operand reads alternating with the B loads
-//              of step t+2;
+//              transposed B writes of step t+1 and the B loads of step t+2;
+//   substep 2: the next substep's operand reads;
 //   substep 3: four MFMAs, the wait + barrier that publishes step t+1's
-//              buffers, then the first operand reads of step t+1.
+//              buffers, then the first operand reads of step t+1 and the A
+//              copies of step t+2 (buffer_load ... lds) into the stage that
+//              the barrier freed.
+// Both operands are thus requested about three substeps before they are
+// needed, which hides an L2 miss.
 // Operand reads are all 128-bit (A and B both K-contiguous in LDS, 16-byte
 // chunks XOR-swizzled by row), and global traffic is issued as inline asm on
 // buffer descriptors that advance in SGPRs, so the compiler adds no waits of
@@ -193,24 +195,24 @@ gemm_scale_relu_ilv_kernel(Problem p)
     };
 
     // One K-step on stage S (the step's A and B are in LDS stage S, its
-    // substep-0 operands are in xf[0]/yf[0]).  t is the step index.
+    // substep-0 operands are in xf[0]/yf[0]).  t is the step index.  Loads run
+    // two steps ahead: B(t+2) is loaded in substep 1 (once the transpose has
+    // freed breg) and A(t+2) is copied into stage S in substep 3 (once the
+    // barrier has freed it), so each has about three substeps of MFMA work to
+    // arrive in.
     auto step = [&](auto stage_tag, int t) {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int SN = S ^ 1;
-        const uint32_t k_next = (uint32_t)(t + 1) * BK;
-        const uint32_t kleft = (k_next < K) ? K - k_next : 0u;  // valid k in step t+1
-        const i32x4 ra = a_rsrc(k_next);
+        const uint32_t k2 = (uint32_t)(t + 2) * BK;
 
-        // substep 0: reads for substep 1 and A copies of step t+1 on
-        // alternating units (one LDS operation per MFMA), then the transpose
+        // substep 0: reads for substep 1 on even units; from unit 8 the
+        // transpose of B(t+1), whose loads are in once at most the 8 copies of
+        // A(t+1) issued after them are still in flight
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mma(i, xf[0], yf[0]);
             if ((i & 1) == 0) read_next(S, 1, i >> 1, xf[1], yf[1]);
-            else copy_a(SN, i >> 1, kleft, ra);
-            // B of step t+1 is in once at most the A copies issued since (units
-            // 1, 3, 5, 7) are still in flight
-            if (i == 8) wait_vmcnt_b<4>(breg);
+            if (i == 8) wait_vmcnt_b<T::A_PER>(breg);
             if (i >= 8) {
                 // 4 of the 32 permutes per unit
                 const int e = (i - 8) >> 1, d0 = ((i - 8) & 1) * 2;
@@ -222,47 +224,57 @@ gemm_scale_relu_ilv_kernel(Problem p)
             }
             sched_fence();
         }
-        // substep 1: reads for substep 2, transposed B stores of step t+1
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            mma(i, xf[1], yf[1]);
-            if ((i & 1) == 0) read_next(S, 2, i >> 1, xf[0], yf[0]);
-            else *(u32x4*)(smem + SN * T::B_BYTES + bw_addr[i >> 1]) = bcol[i >> 1];
-            sched_fence();
-        }
-        // substep 2: reads for substep 3, B loads of step t+2
+        // substep 1: reads for substep 2 on even units; transposed B(t+1)
+        // stores into stage SN and the loads of B(t+2) on odd units
         {
-            const uint32_t k2 = (uint32_t)(t + 2) * BK;
             const i32x4 rb = b_rsrc(k2);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                mma(i, xf[0], yf[0]);
-                if ((i & 1) == 0) read_next(S, 3, i >> 1, xf[1], yf[1]);
-                else breg[i >> 1] = load16(rb, b_voff[i >> 1]);
+                mma(i, xf[1], yf[1]);
+                if ((i & 1) == 0) read_next(S, 2, i >> 1, xf[0], yf[0]);
+                else {
+                    *(u32x4*)(smem + SN * T::B_BYTES + bw_addr[i >> 1]) = bcol[i >> 1];
+                    breg[i >> 1] = load16(rb, b_voff[i >> 1]);
+                }
                 sched_fence();
             }
         }
-        // substep 3: publish step t+1 (its A copies landed; B stores done;
-        // every read of stage S finished), then its substep-0 reads
+        // substep 2: reads for substep 3
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            mma(i, xf[1], yf[1]);
-            if (i == 3) {
-                wait_vmcnt<T::B_LOADS>();
-                lds_barrier();
-            }
-            if (i >= 4 && i < 12) read_next(SN, 0, i - 4, xf[0], yf[0]);
+            mma(i, xf[0], yf[0]);
+            if ((i & 1) == 0) read_next(S, 3, i >> 1, xf[1], yf[1]);
             sched_fence();
+        }
+        // substep 3: publish step t+1 (the copies of A(t+1) landed: only the 8
+        // B(t+2) loads issued after them may be in flight; B(t+1) stores are
+        // done; every read of stage S finished), then the substep-0 reads of
+        // step t+1 and the copies of A(t+2) into the freed stage S
+        {
+            const uint32_t kleft2 = (k2 < K) ? K - k2 : 0u;  // valid k in step t+2
+            const i32x4 ra = a_rsrc(k2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                mma(i, xf[1], yf[1]);
+                if (i == 3) {
+                    wait_vmcnt<T::B_LOADS>();
+                    lds_barrier();
+                }
+                if (i >= 4 && i < 12) {
+                    read_next(SN, 0, i - 4, xf[0], yf[0]);
+                    copy_a(S, i - 4, kleft2, ra);
+                }
+                sched_fence();
+            }
         }
     };
 
-    // ---- prologue: A(0) and B(0) into stage 0, B(1) in flight ----------------
+    // ---- prologue: A(0), B(0) in stage 0; B(1) and then A(1) in flight ------
     const int ksteps = (((int)K + BK - 1) / BK + 1) & ~1;  // even
     {
-        const uint32_t kleft0 = K;
-        const i32x4 ra = a_rsrc(0);
+        const i32x4 ra0 = a_rsrc(0);
 #pragma unroll
-        for (int i = 0; i < T::A_PER; ++i) copy_a(0, i, kleft0, ra);
+        for (int i = 0; i < T::A_PER; ++i) copy_a(0, i, K, ra0);
         const i32x4 rb = b_rsrc(0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) breg[j] = load16(rb, b_voff[j]);
@@ -273,7 +285,10 @@ gemm_scale_relu_ilv_kernel(Problem p)
         const i32x4 rb1 = b_rsrc((uint32_t)BK);
 #pragma unroll
         for (int j = 0; j < 8; ++j) breg[j] = load16(rb1, b_voff[j]);
-        wait_vmcnt<T::B_LOADS>();
+        const uint32_t kleft1 = ((uint32_t)BK < K) ? K - (uint32_t)BK : 0u;
+        const i32x4 ra1 = a_rsrc((uint32_t)BK);
+#pragma unroll
+        for (int i = 0; i < T::A_PER; ++i) copy_a(1, i, kleft1, ra1);
         lds_barrier();
 #pragma unroll
         for (int i = 0; i < 8; ++i) read_next(0, 0, i, xf[0], yf[0]);
