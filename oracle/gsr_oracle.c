@@ -38,6 +38,21 @@
  * accumulator is a Python float, i.e. binary64), round-to-nearest-even for
  * the fp16 narrowing, +0 for every non-positive result, +inf on overflow.
  *
+ * Epilogue variants (the aikraft.ru TileLang guide, section 4 "Слияние
+ * эпилогов: GEMM + Bias + GELU": the matmul result gets a bias added and then
+ * an exp-based GELU approximation, all before the single store):
+ *
+ *     C[m,n] = act( alpha * sum_k A[m,k] B[k,n] + bias[n] )
+ *
+ * with bias an optional fp16 vector over the N output columns and act one of
+ * ReLU, GELU or the identity.  GELU is the tanh form
+ *     gelu(y) = y/2 * (1 + tanh( sqrt(2/pi) * (y + 0.044715 y^3) )),
+ * its tanh taken from exp (the guide names an exponent-based formula).  The
+ * guide fixes neither the bias layout nor the GELU constants; the readings
+ * are: bias per output column, fp16 like the operands, added in the
+ * accumulator precision after the scale; the tanh-form constants above.
+ * Activation codes: 0 ReLU, 1 GELU, 2 identity.
+ *
  * Compile-time switch ORACLE_MUTANT (default 0) plants one deliberate
  * mistake; it exists only so the pin tests can prove that they catch
  * plausible bugs.  A normal build never defines it.
@@ -158,6 +173,62 @@ static double scale_relu(double s, float alpha)
 #endif
 }
 
+#define ORACLE_ACT_RELU 0
+#define ORACLE_ACT_GELU 1
+#define ORACLE_ACT_NONE 2
+
+/* GELU, tanh form: y/2 * (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
+ * tanh comes from t = exp(-2|u|) in (0, 1]: tanh(|u|) = (1 - t)/(1 + t), so
+ *   1 + tanh(u) = 2/(1 + t)      for u >= 0,
+ *   1 + tanh(u) = 2t/(1 + t)     for u <  0,
+ * which avoids the cancellation of 1 + tanh(u) when u is very negative. */
+double oracle_gelu(double y)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+#if ORACLE_MUTANT == 11
+    const double u = c * y; /* mistake: cubic term dropped */
+#else
+    const double u = c * (y + 0.044715 * y * y * y);
+#endif
+    const double t = exp(-2.0 * fabs(u));
+    const double one_plus_tanh = (u >= 0.0) ? 2.0 / (1.0 + t) : 2.0 * t / (1.0 + t);
+    return 0.5 * y * one_plus_tanh;
+}
+
+static double activate(double y, int act)
+{
+    if (act == ORACLE_ACT_RELU) return (y > 0.0) ? y : 0.0; /* -0 and NaN fall to +0 */
+    if (act == ORACLE_ACT_GELU) return oracle_gelu(y);
+    return y;
+}
+
+/* The general epilogue: act(alpha * s + bias), bias = NULL for none. */
+static double epilogue(double s, float alpha, const double* bias_n, int act)
+{
+    if (!bias_n && act == ORACLE_ACT_RELU) return scale_relu(s, alpha);
+#if ORACLE_MUTANT == 9
+    (void)bias_n; /* mistake: bias dropped */
+    return activate((double)alpha * s, act);
+#elif ORACLE_MUTANT == 12
+    return activate((double)alpha * s, act) + (bias_n ? *bias_n : 0.0); /* mistake: bias after act */
+#else
+    return activate((double)alpha * s + (bias_n ? *bias_n : 0.0), act);
+#endif
+}
+
+/* The bias element that output (m, n) takes. */
+static const double* bias_of(const double* biasd, int64_t m, int64_t n)
+{
+    if (!biasd) return NULL;
+#if ORACLE_MUTANT == 10
+    (void)n;
+    return biasd + m; /* mistake: bias indexed by row */
+#else
+    (void)m;
+    return biasd + n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Full mode: every output.  Rows are split over threads; each output sums  */
 /* its products in ascending k.                                             */
@@ -168,8 +239,10 @@ typedef struct {
     const double* Ad; /* decoded A, M*K */
     const double* Bd; /* decoded B, K*N */
     float alpha;
+    const double* biasd; /* decoded bias, N, or NULL */
+    int act;
     uint16_t* C;
-    double* R; /* optional: ReLU(alpha*s) in fp64 before narrowing */
+    double* R; /* optional: the epilogue's value in fp64 before narrowing */
     int64_t row0, row1;
 } full_job;
 
@@ -199,7 +272,7 @@ static void* full_worker(void* p)
 #endif
         }
         for (int64_t n = 0; n < N; ++n) {
-            double r = scale_relu(acc[n], j->alpha);
+            double r = epilogue(acc[n], j->alpha, bias_of(j->biasd, m, n), j->act);
             j->C[m * N + n] = oracle_f64_to_fp16(r);
             if (j->R) j->R[m * N + n] = r;
         }
@@ -208,14 +281,17 @@ static void* full_worker(void* p)
     return NULL;
 }
 
-/* C (and, if R != NULL, the fp64 value before narrowing) for all M x N
- * outputs.  nthreads <= 0 means 1.  Returns ORACLE_OK or an error code. */
-int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                           float alpha, uint16_t* C, double* R, int nthreads)
+/* C = act(alpha * A B + bias) (and, if R != NULL, the fp64 value before
+ * narrowing) for all M x N outputs.  bias: N fp16 values or NULL; act: 0 ReLU,
+ * 1 GELU, 2 identity.  nthreads <= 0 means 1.  Returns ORACLE_OK or an error
+ * code. */
+int oracle_gemm_bias_act(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                         const uint16_t* bias, float alpha, int act, uint16_t* C, double* R, int nthreads)
 {
-    double *Ad = NULL, *Bd = NULL;
+    double *Ad = NULL, *Bd = NULL, *biasd = NULL;
     int rc = ORACLE_OK;
     if (M < 0 || N < 0 || K < 0) return ORACLE_EINVAL;
+    if (act < ORACLE_ACT_RELU || act > ORACLE_ACT_NONE) return ORACLE_EINVAL;
     if (M == 0 || N == 0) return ORACLE_OK;
     if (!C || (K > 0 && (!A || !B))) return ORACLE_EINVAL;
     if (nthreads <= 0) nthreads = 1;
@@ -223,13 +299,16 @@ int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, c
 
     Ad = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
     Bd = (double*)malloc((size_t)(K * N > 0 ? K * N : 1) * sizeof(double));
-    if (!Ad || !Bd) {
+    if (bias) biasd = (double*)malloc((size_t)N * sizeof(double));
+    if (!Ad || !Bd || (bias && !biasd)) {
         free(Ad);
         free(Bd);
+        free(biasd);
         return ORACLE_ENOMEM;
     }
     oracle_decode_array(M * K, A, Ad);
     oracle_decode_array(K * N, B, Bd);
+    if (bias) oracle_decode_array(N, bias, biasd);
 
     {
         full_job* jobs = (full_job*)calloc((size_t)nthreads, sizeof(full_job));
@@ -240,6 +319,7 @@ int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, c
             for (int t = 0; t < nthreads; ++t) {
                 jobs[t].M = M; jobs[t].N = N; jobs[t].K = K;
                 jobs[t].Ad = Ad; jobs[t].Bd = Bd; jobs[t].alpha = alpha;
+                jobs[t].biasd = biasd; jobs[t].act = act;
                 jobs[t].C = C; jobs[t].R = R;
                 jobs[t].row0 = M * t / nthreads;
                 jobs[t].row1 = M * (t + 1) / nthreads;
@@ -257,7 +337,15 @@ int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, c
     }
     free(Ad);
     free(Bd);
+    free(biasd);
     return rc;
+}
+
+/* The tutorial's operation: C = ReLU(alpha * A B). */
+int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                           float alpha, uint16_t* C, double* R, int nthreads)
+{
+    return oracle_gemm_bias_act(M, N, K, A, B, NULL, alpha, ORACLE_ACT_RELU, C, R, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -268,8 +356,9 @@ int oracle_gemm_scale_relu(int64_t M, int64_t N, int64_t K, const uint16_t* A, c
 
 typedef struct {
     int64_t M, N, K;
-    const uint16_t *A, *B;
+    const uint16_t *A, *B, *bias;
     float alpha;
+    int act;
     const int64_t *ms, *ns;
     uint16_t* out;
     double* R;
@@ -300,7 +389,17 @@ static void* point_worker(void* p)
 #endif
         }
         {
-            double r = scale_relu(s, j->alpha);
+            double bd = 0.0;
+            const double* bp = NULL;
+            if (j->bias) {
+#if ORACLE_MUTANT == 10
+                bd = oracle_fp16_to_f64(j->bias[m]); /* mistake: bias indexed by row */
+#else
+                bd = oracle_fp16_to_f64(j->bias[n]);
+#endif
+                bp = &bd;
+            }
+            double r = epilogue(s, j->alpha, bp, j->act);
             j->out[i] = oracle_f64_to_fp16(r);
             if (j->R) j->R[i] = r;
         }
@@ -308,12 +407,14 @@ static void* point_worker(void* p)
     return NULL;
 }
 
-/* Outputs C[ms[i], ns[i]] for i < npts.  Indices must lie in [0,M) x [0,N). */
-int oracle_gemm_scale_relu_points(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
-                                  float alpha, int64_t npts, const int64_t* ms, const int64_t* ns,
-                                  uint16_t* out, double* R, int nthreads)
+/* Outputs C[ms[i], ns[i]] of act(alpha * A B + bias) for i < npts.  Indices
+ * must lie in [0,M) x [0,N); bias (N values) may be NULL. */
+int oracle_gemm_bias_act_points(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                                const uint16_t* bias, float alpha, int act, int64_t npts, const int64_t* ms,
+                                const int64_t* ns, uint16_t* out, double* R, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0 || npts < 0) return ORACLE_EINVAL;
+    if (act < ORACLE_ACT_RELU || act > ORACLE_ACT_NONE) return ORACLE_EINVAL;
     if (npts == 0) return ORACLE_OK;
     if (!ms || !ns || !out || (K > 0 && (!A || !B))) return ORACLE_EINVAL;
     for (int64_t i = 0; i < npts; ++i)
@@ -330,7 +431,7 @@ int oracle_gemm_scale_relu_points(int64_t M, int64_t N, int64_t K, const uint16_
         }
         for (int t = 0; t < nthreads; ++t) {
             jobs[t].M = M; jobs[t].N = N; jobs[t].K = K;
-            jobs[t].A = A; jobs[t].B = B; jobs[t].alpha = alpha;
+            jobs[t].A = A; jobs[t].B = B; jobs[t].bias = bias; jobs[t].alpha = alpha; jobs[t].act = act;
             jobs[t].ms = ms; jobs[t].ns = ns; jobs[t].out = out; jobs[t].R = R;
             jobs[t].i0 = npts * t / nthreads;
             jobs[t].i1 = npts * (t + 1) / nthreads;
@@ -342,6 +443,14 @@ int oracle_gemm_scale_relu_points(int64_t M, int64_t N, int64_t K, const uint16_
         free(th);
     }
     return ORACLE_OK;
+}
+
+/* The tutorial's operation at chosen outputs. */
+int oracle_gemm_scale_relu_points(int64_t M, int64_t N, int64_t K, const uint16_t* A, const uint16_t* B,
+                                  float alpha, int64_t npts, const int64_t* ms, const int64_t* ns,
+                                  uint16_t* out, double* R, int nthreads)
+{
+    return oracle_gemm_bias_act_points(M, N, K, A, B, NULL, alpha, ORACLE_ACT_RELU, npts, ms, ns, out, R, nthreads);
 }
 
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }

@@ -18,9 +18,18 @@ What pins what:
   * invariants -- outputs are never negative, flipping alpha's sign zeroes
     every output that was positive, doubling alpha doubles outputs,
     transposition, permutation of k, zero padding;
-  * hand-worked examples in tests/golden/worked_examples.txt.
+  * hand-worked examples in tests/golden/worked_examples.txt;
+  * the epilogue variants (bias per output column; ReLU, GELU or nothing):
+    GELU against the tanh form as usually written with the library tanh,
+    against the exact GELU x*Phi(x) from the library erf (the tanh form is an
+    approximation of it to 5e-4), and its odd-part identity
+    gelu(y) - gelu(-y) = y; bias and activation against exact rationals; K=0
+    and zero-bias closed forms; the identity that a bias equals one more k
+    term (a column of ones in A, the bias as a row of B).
 The operation itself: PKUHPC scow-tutorial "Tutorial14", section 3, display
 formula; the listing in section 2 fixes scale-then-max and the fp16 output.
+The epilogue variants: the aikraft.ru TileLang guide, section 4 (GEMM + Bias
++ GELU, with an exponent-based GELU approximation).
 """
 from __future__ import annotations
 
@@ -364,4 +373,169 @@ def pin_golden(orc) -> List[str]:
     return fails
 
 
-ALL_PINS = [pin_decode, pin_encode, pin_bruteforce, pin_closed_forms, pin_invariants, pin_golden]
+# ---------------------------------------------------------------------------
+# Epilogue variants: C = act(alpha * A B + bias[n])
+# ---------------------------------------------------------------------------
+
+ACT_RELU, ACT_GELU, ACT_NONE = 0, 1, 2
+ACTS = (ACT_RELU, ACT_GELU, ACT_NONE)
+_GELU_C = math.sqrt(2.0 / math.pi)
+
+
+def gelu_textbook(y: float) -> float:
+    """The tanh form of GELU as it is usually written, with the library tanh."""
+    return 0.5 * y * (1.0 + math.tanh(_GELU_C * (y + 0.044715 * y ** 3)))
+
+
+def gelu_exact(y: float) -> float:
+    """GELU itself: y * Phi(y), Phi the standard normal CDF via erf."""
+    return 0.5 * y * (1.0 + math.erf(y / math.sqrt(2.0)))
+
+
+def _fp16_ulps_apart(x: int, y: int) -> int:
+    """Distance in representable steps between two fp16 bit patterns."""
+    def key(b):
+        b = int(b)
+        return -(b & 0x7FFF) if b & 0x8000 else b
+    return abs(key(x) - key(y))
+
+
+def exact_reference_bias_act(a_bits, b_bits, bias_bits, alpha, act):
+    """C bits of act(alpha * A B + bias) for tiny shapes: the sum, scale and
+    bias in exact rationals; ReLU and the identity exact too; GELU of the
+    exact value rounded once to binary64, by the textbook formula."""
+    M, K = a_bits.shape
+    N = b_bits.shape[1]
+    A = [[Fraction(fp16_value(a_bits[m, k])) for k in range(K)] for m in range(M)]
+    B = [[Fraction(fp16_value(b_bits[k, n])) for n in range(N)] for k in range(K)]
+    bias = [Fraction(fp16_value(bias_bits[n])) if bias_bits is not None else Fraction(0) for n in range(N)]
+    al = Fraction(float(np.float32(alpha)))
+    out = np.zeros((M, N), dtype=np.uint16)
+    exact = {}
+    for m in range(M):
+        for n in range(N):
+            y = al * sum((A[m][k] * B[k][n] for k in range(K)), Fraction(0)) + bias[n]
+            exact[m, n] = y
+            if act == ACT_RELU:
+                out[m, n] = fraction_to_fp16_bits(y if y > 0 else Fraction(0))
+            elif act == ACT_NONE:
+                out[m, n] = fraction_to_fp16_bits(y)
+            else:
+                out[m, n] = fraction_to_fp16_bits(Fraction(gelu_textbook(float(y))))
+    return out, exact
+
+
+def pin_gelu(orc) -> List[str]:
+    fails: List[str] = []
+    rng = np.random.Generator(np.random.PCG64(2024))
+    ys = np.concatenate([np.linspace(-12.0, 12.0, 8001), rng.standard_normal(20000) * 4.0,
+                         [0.0, -0.0, 1e-300, -1e-300, 1e-8, -1e-8, 30.0, -30.0]])
+    worst_t = worst_e = worst_s = 0.0
+    for y in ys:
+        g = orc.gelu(float(y))
+        worst_t = max(worst_t, abs(g - gelu_textbook(float(y))) / max(1.0, abs(y)))
+        worst_e = max(worst_e, abs(g - gelu_exact(float(y))))
+        worst_s = max(worst_s, abs(g - orc.gelu(-float(y)) - y) / max(1.0, abs(y)))
+    if worst_t > 4e-15:
+        fails.append(f"gelu: differs from the textbook tanh form by {worst_t:.3g} (relative)")
+    if worst_e > 5e-4:
+        fails.append(f"gelu: differs from y*Phi(y) by {worst_e:.3g} (the tanh form is within 4.8e-4)")
+    if worst_s > 4e-15:
+        fails.append(f"gelu: gelu(y) - gelu(-y) differs from y by {worst_s:.3g}")
+    if orc.gelu(0.0) != 0.0 or orc.gelu(60.0) != 60.0 or abs(orc.gelu(-60.0)) > 1e-300:
+        fails.append("gelu: wrong at 0 or in the tails")
+    return fails
+
+
+def pin_bias_act_bruteforce(orc, seed=11) -> List[str]:
+    """Bias and activation against exact rationals (M <= N everywhere, so a
+    bias indexed by row would still stay inside the bias array).  ReLU and
+    the identity must be bit-exact unless the fp64 error bound straddles a
+    rounding midpoint; GELU (a transcendental of the exact sum) may differ by
+    one fp16 step."""
+    fails: List[str] = []
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = [(1, 3, 2), (2, 5, 3), (3, 7, 5), (4, 4, 17), (5, 13, 8), (2, 17, 1), (3, 3, 0), (6, 9, 13)]
+    for ci, (M, N, K) in enumerate(cases):
+        a = random_fp16_bits(rng, (M, K))
+        b = random_fp16_bits(rng, (K, N))
+        bias = random_fp16_bits(rng, (N,), 2.0)
+        for alpha in (1.0, 0.5, -0.75):
+            for act in ACTS:
+                want, exact = exact_reference_bias_act(a, b, bias, alpha, act)
+                got, _ = orc.gemm_bias_act(a, b, bias, alpha, act, nthreads=1)
+                gp, _ = orc.gemm_bias_act_points(a, b, bias, alpha, act, *np.divmod(np.arange(M * N), N), nthreads=2)
+                for name, g in (("full", got), ("points", gp.reshape(M, N))):
+                    for (m, n) in np.argwhere(g != want):
+                        if act == ACT_GELU:
+                            if _fp16_ulps_apart(g[m, n], want[m, n]) <= 1:
+                                continue
+                        else:
+                            av = np.abs(a[m].view(np.float16).astype(np.float64))
+                            bv = np.abs(b[:, n].view(np.float16).astype(np.float64))
+                            bound = Fraction((K + 2) * 2.0 ** -53 * (abs(alpha) * float(np.dot(av, bv))
+                                                                    + abs(fp16_value(bias[n]))))
+                            y = exact[m, n]
+                            lo, hi = y - bound, y + bound
+                            if act == ACT_RELU:
+                                lo, hi = max(lo, Fraction(0)), max(hi, Fraction(0))
+                            if fraction_to_fp16_bits(lo) != fraction_to_fp16_bits(hi):
+                                continue
+                        fails.append(f"bias/act {name} case {ci} {(M, N, K)} alpha={alpha} act={act} at "
+                                     f"{(int(m), int(n))}: 0x{int(g[m, n]):04x} != 0x{int(want[m, n]):04x}")
+                        break
+    return fails
+
+
+def pin_bias_act_forms(orc, seed=13) -> List[str]:
+    fails: List[str] = []
+    rng = np.random.Generator(np.random.PCG64(seed))
+    M, N, K = 7, 11, 29
+    a = random_fp16_bits(rng, (M, K))
+    b = random_fp16_bits(rng, (K, N))
+    bias = random_fp16_bits(rng, (N,), 3.0)
+    bv = bias.view(np.float16).astype(np.float64)
+    # K = 0: every output is act(bias[n]), the empty sum plus the bias
+    for act in ACTS:
+        c, _ = orc.gemm_bias_act(np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), bias, 0.5, act)
+        if act == ACT_RELU:
+            _cmp("bias K=0 relu", c, np.tile(to_bits(np.where(bv > 0, bv, 0.0)), (M, 1)), fails)
+        elif act == ACT_NONE:
+            _cmp("bias K=0 identity", c, np.tile(bias, (M, 1)), fails)
+        else:
+            want = to_bits([gelu_textbook(float(v)) for v in bv])
+            if any(_fp16_ulps_apart(x, y) > 1 for x, y in zip(c[0], want)) or np.any(c != c[0]):
+                fails.append("bias K=0 gelu: not gelu(bias) in every row")
+    # no bias, ReLU: the tutorial's operation; a zero bias changes nothing
+    c0, _ = orc.gemm_scale_relu(a, b, 0.5)
+    c1, _ = orc.gemm_bias_act(a, b, None, 0.5, ACT_RELU)
+    c2, _ = orc.gemm_bias_act(a, b, np.zeros(N, np.uint16), 0.5, ACT_RELU)
+    _cmp("bias None == scale_relu", c1, c0, fails)
+    _cmp("zero bias == no bias", c2, c0, fails)
+    # a bias is one more k term: A gets a column of ones, B the row bias/alpha
+    # (alpha a power of two, so bias/alpha is exact in fp16)
+    for alpha in (1.0, 0.5):
+        aa = np.concatenate([a, np.full((M, 1), 0x3C00, np.uint16)], axis=1)
+        ba = np.concatenate([b, to_bits(bv / alpha)[None, :]], axis=0)
+        for act in ACTS:
+            cb, _ = orc.gemm_bias_act(a, b, bias, alpha, act)
+            ck, _ = orc.gemm_bias_act(aa, ba, None, alpha, act)
+            _cmp(f"bias == extra k term alpha={alpha} act={act}", cb, ck, fails)
+    # the identity activation is signed; ReLU of it is the ReLU variant
+    cn, rn = orc.gemm_bias_act(a, b, bias, 0.5, ACT_NONE, want_fp64=True)
+    cr, _ = orc.gemm_bias_act(a, b, bias, 0.5, ACT_RELU)
+    _cmp("relu == max(identity, 0)", cr, to_bits(np.where(rn > 0, rn, 0.0)), fails)
+    if not np.any(cn & 0x8000):
+        fails.append("identity activation produced no negative output")
+    # points agree with full mode
+    ms = rng.integers(0, M, 40)
+    ns = rng.integers(0, N, 40)
+    for act in ACTS:
+        cf, _ = orc.gemm_bias_act(a, b, bias, 0.5, act)
+        cp, _ = orc.gemm_bias_act_points(a, b, bias, 0.5, act, ms, ns)
+        _cmp(f"bias points == full act={act}", cp, cf[ms, ns], fails)
+    return fails
+
+
+ALL_PINS = [pin_decode, pin_encode, pin_bruteforce, pin_closed_forms, pin_invariants, pin_golden,
+            pin_gelu, pin_bias_act_bruteforce, pin_bias_act_forms]

@@ -1,7 +1,9 @@
 """Each planted mistake in the oracle (compile-time ORACLE_MUTANT) must be
 caught by at least one pin: a dropped k term, A read column-major, truncating
 instead of rounding, ReLU before the scale, the scale dropped, subnormals
-decoded as normals, ties rounded away from zero, a binary32 running sum."""
+decoded as normals, ties rounded away from zero, a binary32 running sum, and
+in the epilogue variants a dropped bias, a bias indexed by row, GELU without
+its cubic term, the bias added after the activation."""
 import os
 
 import pytest
@@ -17,6 +19,10 @@ MUTANTS = {
     6: "subnormal inputs decoded with an implicit 1",
     7: "ties rounded away from zero",
     8: "binary32 running sum",
+    9: "bias dropped",
+    10: "bias indexed by row instead of column",
+    11: "GELU without the cubic term",
+    12: "bias added after the activation",
 }
 
 
