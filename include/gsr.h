@@ -50,6 +50,13 @@ enum gsr_status {
     GSR_ERROR_INVALID_CONFIG = 6      /* gemm_scale_relu_ex: unknown config id */
 };
 
+/* Activation of the epilogue variants. */
+enum gsr_activation {
+    GSR_ACT_RELU = 0, /* max(v, 0); non-positive results are +0 */
+    GSR_ACT_GELU = 1, /* v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3))) */
+    GSR_ACT_NONE = 2  /* v itself */
+};
+
 /* One compiled tile configuration.  A workgroup of waves_m*waves_n wave64s
  * owns a block_m x block_n tile of C and walks K in steps of block_k through
  * `stages` LDS buffers; each wave owns a (block_m/waves_m) x (block_n/waves_n)
@@ -81,6 +88,33 @@ int gemm_scale_relu(int64_t M, int64_t N, int64_t K,
 int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K,
                        const void* A, const void* B, void* C,
                        float alpha, void* stream, int32_t config_id);
+
+/* The epilogue variants (the aikraft.ru TileLang guide, section 4 "Слияние
+ * эпилогов: GEMM + Bias + GELU": a bias and an exponent-based GELU applied to
+ * the matmul result in registers before the single store):
+ *
+ *     C[m,n] = act( alpha * sum_{k<K} A[m,k] * B[k,n] + bias[n] )
+ *
+ *   bias  NULL, or N IEEE binary16 values on the device (one per output
+ *         column, at least 2-byte aligned; 8-byte alignment keeps the 128-bit
+ *         path), read-only, must not overlap C
+ *   activation  a gsr_activation; GELU is the tanh form, evaluated in binary32
+ *         as v / (1 + exp(-2u)), u = sqrt(2/pi) (v + 0.044715 v^3)
+ * The sum, the scale, the bias and the activation are binary32; one
+ * round-to-nearest-even narrowing to binary16.  With bias == NULL and
+ * GSR_ACT_RELU this is exactly gemm_scale_relu; the guide's GEMM + Bias + GELU
+ * is alpha = 1, GSR_ACT_GELU.  K == 0 gives act(bias[n]) (+0 without a bias).
+ * Layout, alignment, ownership and errors as gemm_scale_relu; in addition
+ * GSR_ERROR_INVALID_VALUE for an unknown activation, an odd bias address or
+ * a bias overlapping C. */
+int gemm_scale_bias_act(int64_t M, int64_t N, int64_t K,
+                        const void* A, const void* B, const void* bias, void* C,
+                        float alpha, int32_t activation, void* stream);
+
+/* As gemm_scale_bias_act with a forced tile configuration (-1 = selector). */
+int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K,
+                           const void* A, const void* B, const void* bias, void* C,
+                           float alpha, int32_t activation, void* stream, int32_t config_id);
 
 /* The configuration the selector picks for an M x N x K problem.  Host only;
  * touches no device.  Returns GSR_SUCCESS or GSR_ERROR_INVALID_VALUE. */

@@ -38,6 +38,19 @@ def run_gpu(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id: int = -1,
     return W.fp16_bits(out.cpu())
 
 
+def run_gpu_variant(a: torch.Tensor, b: torch.Tensor, bias, alpha: float, act: str,
+                    config_id: int = -1, c: torch.Tensor = None) -> np.ndarray:
+    """act(alpha * a @ b + bias) through the epilogue-variant entry point.
+    a, b, bias (or None): CPU fp16 tensors.  Returns C's bit patterns."""
+    import tiled_dense_gemm_scale_amd as gsr
+
+    dev = torch.device("cuda:0")
+    bd = bias.to(dev) if bias is not None else None
+    out = gsr.gemm_scale_bias_act(a.to(dev), b.to(dev), bd, alpha, act, c=c, config_id=config_id)
+    torch.cuda.synchronize()
+    return W.fp16_bits(out.cpu())
+
+
 class Report:
     def __init__(self, name, n, max_abs, max_rel_excess, violations, worst, fro):
         self.name, self.n, self.max_abs = name, n, max_abs

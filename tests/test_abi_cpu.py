@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gemm_scale_relu", "gemm_scale_relu_ex", "gsr_select_config", "gsr_num_configs",
-              "gsr_get_config", "gsr_status_string", "gsr_version"):
+    for n in ("gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "gemm_scale_bias_act_ex",
+              "gsr_select_config", "gsr_num_configs", "gsr_get_config", "gsr_status_string", "gsr_version"):
         assert n in names
 
 
@@ -103,6 +103,29 @@ def test_nonfinite_alpha_and_bad_config(native):
     assert native.gemm_scale_relu(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, math.inf, 0) == 1
     assert native.gemm_scale_relu_ex(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, 0, 99) == 6
     assert native.gemm_scale_relu_ex(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, 0, -2) == 6
+
+
+@pytest.mark.parametrize("bias,act", [
+    (FAKE + 12288, 3),          # unknown activation
+    (FAKE + 12288, -1),
+    (FAKE + 12289, 1),          # odd bias address
+    (FAKE + 8192 + 8, 1),       # bias inside C (C is 4x4 fp16 = 32 bytes at FAKE+8192)
+    (FAKE + 8192 - 4, 2),       # bias (4 values, 8 bytes) running into C's first bytes
+])
+def test_epilogue_argument_errors(native, bias, act):
+    # every case is rejected on the host, before any device is touched
+    assert native.gemm_scale_bias_act(4, 4, 4, FAKE, FAKE + 4096, bias, FAKE + 8192, 1.0, act, 0) == 1
+
+
+def test_epilogue_variants_share_the_checks(native):
+    import math
+    # the same validation as the plain entry point, before any device work
+    assert native.gemm_scale_bias_act(-1, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 1, 0) == 1
+    assert native.gemm_scale_bias_act(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 16, 1.0, 1, 0) == 1
+    assert native.gemm_scale_bias_act(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, math.nan, 1, 0) == 1
+    assert native.gemm_scale_bias_act(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 1, 0, 99) == 6
+    assert native.gemm_scale_bias_act(0, 4, 4, 0, 0, 0, 0, 1.0, 1, 0) == 0
+    assert native.gemm_scale_bias_act(2 ** 31, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 1, 0) == 2
 
 
 def test_empty_output_is_a_noop(native):

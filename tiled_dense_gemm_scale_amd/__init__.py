@@ -6,6 +6,13 @@ fp32 accumulation, scale and ReLU applied to the fp32 sum in registers, one
 fp16 store (PKUHPC scow-tutorial "Tutorial14", section 3 display formula;
 section 2 listing for the types and the epilogue order).
 
+    C = act(alpha * A @ B + bias)    gemm_scale_bias_act: bias (N,) fp16 or
+                                     None; act "relu", "gelu" (tanh form) or
+                                     "none"
+
+is the epilogue-variant family (the aikraft.ru TileLang guide, section 4,
+GEMM + Bias + GELU) on the same kernels.
+
 The compute runs in libgsr.so's hand-written HIP kernels; this package only
 marshals torch tensors (device memory and the current stream) into the C ABI
 of include/gsr.h.
@@ -19,8 +26,10 @@ import torch
 from . import _native
 from ._native import GsrError, get_config, num_configs, select_config, status_string, version
 
-__all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "GsrError", "select_config", "get_config",
-           "num_configs", "status_string", "version", "configs"]
+__all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "GsrError", "select_config",
+           "get_config", "num_configs", "status_string", "version", "configs", "ACTIVATIONS"]
+
+ACTIVATIONS = {"relu": _native.GSR_ACT_RELU, "gelu": _native.GSR_ACT_GELU, "none": _native.GSR_ACT_NONE}
 
 
 def _check_operands(a: torch.Tensor, b: torch.Tensor, c: Optional[torch.Tensor]):
@@ -68,6 +77,28 @@ def gemm_scale_relu_ex(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id
         s = _stream_handle(a.device, stream)
         st = _native.gemm_scale_relu_ex(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), alpha, s,
                                         config_id)
+    _native.check(st)
+    return c
+
+
+def gemm_scale_bias_act(a: torch.Tensor, b: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                        alpha: float = 1.0, activation: str = "relu", c: Optional[torch.Tensor] = None,
+                        stream=None, config_id: int = -1) -> torch.Tensor:
+    """C = act(alpha * a @ b + bias), bias one fp16 value per output column
+    (or None), act "relu", "gelu" or "none"; enqueued on `stream`.  With
+    bias=None and "relu" it is gemm_scale_relu.  Returns C."""
+    M, N, K, c = _check_operands(a, b, c)
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
+    bptr = 0
+    if bias is not None:
+        if bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous ({N},) float16 device tensor")
+        bptr = bias.data_ptr()
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_bias_act(M, N, K, a.data_ptr(), b.data_ptr(), bptr, c.data_ptr(), alpha,
+                                         ACTIVATIONS[activation], s, config_id)
     _native.check(st)
     return c
 

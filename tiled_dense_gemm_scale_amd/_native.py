@@ -20,6 +20,10 @@ GSR_ERROR_UNSUPPORTED_DEVICE = 4
 GSR_ERROR_LAUNCH = 5
 GSR_ERROR_INVALID_CONFIG = 6
 
+GSR_ACT_RELU = 0
+GSR_ACT_GELU = 1
+GSR_ACT_NONE = 2
+
 
 class GsrConfig(ctypes.Structure):
     """Mirror of struct gsr_config."""
@@ -67,6 +71,10 @@ def lib() -> ctypes.CDLL:
             L.gemm_scale_relu.restype = ctypes.c_int
             L.gemm_scale_relu_ex.argtypes = [i64, i64, i64, vp, vp, vp, f32, vp, i32]
             L.gemm_scale_relu_ex.restype = ctypes.c_int
+            L.gemm_scale_bias_act.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp]
+            L.gemm_scale_bias_act.restype = ctypes.c_int
+            L.gemm_scale_bias_act_ex.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, i32]
+            L.gemm_scale_bias_act_ex.restype = ctypes.c_int
             L.gsr_select_config.argtypes = [i64, i64, i64, ctypes.POINTER(GsrConfig)]
             L.gsr_select_config.restype = ctypes.c_int
             L.gsr_num_configs.argtypes = []
@@ -100,6 +108,14 @@ def gemm_scale_relu_ex(M: int, N: int, K: int, A: int, B: int, C: int, alpha: fl
                        config_id: int) -> int:
     return lib().gemm_scale_relu_ex(M, N, K, A or None, B or None, C or None, float(alpha),
                                     stream or None, int(config_id))
+
+
+def gemm_scale_bias_act(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, alpha: float,
+                        activation: int, stream: int, config_id: int = -1) -> int:
+    """Raw entry point of the epilogue variants (bias 0 = none).  Returns the
+    gsr_status."""
+    return lib().gemm_scale_bias_act_ex(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
+                                        int(activation), stream or None, int(config_id))
 
 
 def select_config(M: int, N: int, K: int) -> dict:

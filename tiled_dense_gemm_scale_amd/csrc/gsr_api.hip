@@ -232,7 +232,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 100; }
+int gsr_version(void) { return 200; }
 
 const char* gsr_status_string(int status)
 {
@@ -265,12 +265,19 @@ int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out)
     return GSR_SUCCESS;
 }
 
-int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, float alpha,
-                       void* stream, int32_t config_id)
+int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                           void* C, float alpha, int32_t activation, void* stream, int32_t config_id)
 {
     int st = validate(M, N, K, A, B, C);
     if (st != GSR_SUCCESS) return st;
     if (!std::isfinite(alpha)) return GSR_ERROR_INVALID_VALUE;
+    if (activation != GSR_ACT_RELU && activation != GSR_ACT_GELU && activation != GSR_ACT_NONE)
+        return GSR_ERROR_INVALID_VALUE;
+    if (bias != nullptr) {
+        // read while C is written: it must not overlap C
+        if ((uintptr_t)bias & 1u) return GSR_ERROR_INVALID_VALUE;
+        if (overlaps(bias, (uint64_t)N * 2u, C, (uint64_t)M * (uint64_t)N * 2u)) return GSR_ERROR_INVALID_VALUE;
+    }
     if (config_id < -1 || config_id >= kNumConfigs) return GSR_ERROR_INVALID_CONFIG;
     if (M == 0 || N == 0) return GSR_SUCCESS;
     st = check_device();
@@ -280,7 +287,8 @@ int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K, const void* A, const voi
     if (K == 0) {
         const uint32_t count = (uint32_t)(M * N);
         const int grid = (int)std::min<int64_t>(cdiv(count, 256), 4096);
-        hipLaunchKernelGGL(gsr::fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint16_t*)C, count);
+        hipLaunchKernelGGL(gsr::fill_epilogue_kernel, dim3(grid), dim3(256), 0, s, (uint16_t*)C, (uint32_t)M,
+                           (uint32_t)N, (const uint16_t*)bias, alpha, (int)activation);
         return hipGetLastError() == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
     }
 
@@ -289,25 +297,40 @@ int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K, const void* A, const voi
     p.A = (const uint16_t*)A;
     p.B = (const uint16_t*)B;
     p.C = (uint16_t*)C;
+    p.bias = (const uint16_t*)bias;
     p.M = (int)M;
     p.N = (int)N;
     p.K = (int)K;
     p.alpha = alpha;
+    p.act = (int)activation;
     p.tiles_m = (int)cdiv(M, e.cfg.block_m);
     p.tiles_n = (int)cdiv(N, e.cfg.block_n);
     p.group_m = e.cfg.group_m;
     p.xcd_remap = e.cfg.xcd_remap;
     const int grid = p.tiles_m * p.tiles_n;
     const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
-                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 7u) == 0);
+                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 7u) == 0) &&
+                     (((uintptr_t)bias & 7u) == 0);
     const hipError_t err = (vec ? e.vec : e.elem)(p, grid, s);
     return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
+}
+
+int gemm_scale_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                        void* C, float alpha, int32_t activation, void* stream)
+{
+    return gemm_scale_bias_act_ex(M, N, K, A, B, bias, C, alpha, activation, stream, -1);
+}
+
+int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, float alpha,
+                       void* stream, int32_t config_id)
+{
+    return gemm_scale_bias_act_ex(M, N, K, A, B, nullptr, C, alpha, GSR_ACT_RELU, stream, config_id);
 }
 
 int gemm_scale_relu(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, float alpha,
                     void* stream)
 {
-    return gemm_scale_relu_ex(M, N, K, A, B, C, alpha, stream, -1);
+    return gemm_scale_bias_act_ex(M, N, K, A, B, nullptr, C, alpha, GSR_ACT_RELU, stream, -1);
 }
 
 }  // extern "C"

@@ -304,30 +304,54 @@ gemm_scale_relu_ilv_kernel(Problem p)
     wait_vmcnt_b<0>(breg);
 
     // ---- epilogue ------------------------------------------------------------
-    // Scale, ReLU and round in registers, then pass the wave's 128x128 fp16
-    // sub-tile through its own 32 KB of LDS so that the global stores write
-    // whole 256-byte row segments (16 lanes per row) instead of 16 bytes in
-    // each of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at
+    // Scale, ReLU (or the variant: scale, bias, activation) and round in
+    // registers, then pass the wave's 128x128 fp16 sub-tile through its own
+    // 32 KB of LDS so that the global stores write whole 256-byte row
+    // segments (16 lanes per row) instead of 16 bytes in each of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at
     // physical chunk c ^ (r % 16).
     static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
     lds_barrier();  // every wave is past its last operand read
     const float alpha = p.alpha;
     uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
+    auto stage4 = [&](int a, int b, int g, half4 h) {
+        const uint32_t r = (uint32_t)b * 32u + frow;
+        const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
+        *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
+    };
+    if (plain_epilogue(p)) {
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
-        for (int b = 0; b < TM; ++b) {
-            const uint32_t r = (uint32_t)b * 32u + frow;
+            for (int b = 0; b < TM; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    half4 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = acc[a][b][4 * g + i] * alpha;
+                        h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                    }
+                    stage4(a, b, g, h);
+                }
+            }
+        }
+    } else {
+        // bias of the lane's four columns, then act(alpha * acc + bias)
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const int act = p.act;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                half4 h;
+                const f32x4 bv = bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = acc[a][b][4 * g + i] * alpha;
-                    h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                for (int b = 0; b < TM; ++b) {
+                    const f32x16 av = acc[a][b];
+                    f32x4 sv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                    stage4(a, b, g, epilogue4(sv, alpha, bv, act));
                 }
-                const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
-                *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
             }
         }
     }

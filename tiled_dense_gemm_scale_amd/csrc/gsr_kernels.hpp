@@ -100,12 +100,76 @@ struct Problem {
     const uint16_t* A;
     const uint16_t* B;
     uint16_t* C;
+    const uint16_t* bias;  // N fp16 values, or null
     int M, N, K;
     float alpha;
+    int act;               // kActRelu, kActGelu or kActNone
     int tiles_m, tiles_n;
     int group_m;
     int xcd_remap;
 };
+
+// ---- epilogue -----------------------------------------------------------
+// The tutorial's epilogue is v = alpha * acc, max(v, 0), narrow.  The
+// epilogue variants (the aikraft.ru TileLang guide, section 4, GEMM + Bias +
+// GELU) add one fp16 bias value per output column after the scale and apply
+// ReLU, the tanh-form GELU or nothing: v = act(alpha * acc + bias[n]).
+enum : int { kActRelu = 0, kActGelu = 1, kActNone = 2 };
+
+// GELU, tanh form: y/2 (1 + tanh(u)) = y / (1 + exp(-2u)) with
+// u = sqrt(2/pi) (y + 0.044715 y^3).  exp(-2u) overflowing to +inf (very
+// negative y) gives -0, underflowing to 0 (large y) gives y.
+__device__ __forceinline__ float gelu_tanh(float y)
+{
+    const float u = 0.7978845608028654f * (y + 0.044715f * (y * y * y));
+    return y / (1.0f + __expf(-2.0f * u));
+}
+
+__device__ __forceinline__ float activate(float y, int act)
+{
+    if (act == kActRelu) return y > 0.0f ? y : 0.0f;
+    if (act == kActGelu) return gelu_tanh(y);
+    return y;
+}
+
+// True when the epilogue is the tutorial's (no bias, ReLU): kernels keep a
+// separate loop for it.
+__device__ __forceinline__ bool plain_epilogue(const Problem& p) { return p.bias == nullptr && p.act == kActRelu; }
+
+// The bias of columns n..n+3 (n a multiple of 4, bias 8-byte aligned, N a
+// multiple of 8: the four are all inside or all outside; outside reads 0).
+__device__ __forceinline__ f32x4 bias4(__amdgpu_buffer_rsrc_t rbias, int n)
+{
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rbias, (uint32_t)n * 2u, 0, 0);
+    const half4 h = __builtin_bit_cast(half4, w);
+    f32x4 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = (float)h[i];
+    return f;
+}
+
+// The bias of column n alone (any alignment; outside reads 0).
+__device__ __forceinline__ float bias1(__amdgpu_buffer_rsrc_t rbias, int n)
+{
+    const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(rbias, (uint32_t)n * 2u, 0, 0);
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// A descriptor over the bias (zero records when there is none).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const Problem& p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.bias), (short)0,
+                                             p.bias ? p.N * 2 : 0, 0x00020000);
+}
+
+// act(alpha * s + b) for four outputs, narrowed to fp16 (round to nearest even).
+__device__ __forceinline__ half4 epilogue4(f32x4 s, float alpha, f32x4 b, int act)
+{
+    half4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = (_Float16)activate(s[i] * alpha + b[i], act);
+    return h;
+}
 
 // Workgroup id -> (tile row, tile column).
 __device__ __forceinline__ void tile_of(int pid, int nwg, const Problem& p, int& tm, int& tn)
@@ -303,44 +367,84 @@ gemm_scale_relu_kernel(Problem p)
     // Accumulator block (a, b): lane l holds m = l % 32 and, in register
     // 4g + i, n = 8g + 4*(l/32) + i.
     const float alpha = p.alpha;
+    auto store4 = [&](int m, int n, half4 h) {
+        const u32x2 w = __builtin_bit_cast(u32x2, h);
+        const uint32_t elem = (uint32_t)m * (uint32_t)p.N + (uint32_t)n;
+        if constexpr (VEC) {
+            const uint32_t off = ((m < p.M) & (n < p.N)) ? elem * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+        } else {
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = ((m < p.M) & (n + i < p.N)) ? (elem + i) * 2u : kOutOfRange;
+                const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
+                __builtin_amdgcn_raw_buffer_store_b16(hv, rc, off, 0, 0);
+            }
+        }
+    };
+    if (plain_epilogue(p)) {
 #pragma unroll
-        for (int b = 0; b < TM; ++b) {
-            const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+        for (int a = 0; a < TN; ++a) {
+#pragma unroll
+            for (int b = 0; b < TM; ++b) {
+                const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
+                    half4 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = acc[a][b][4 * g + i] * alpha;
+                        h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                    }
+                    store4(m, n, h);
+                }
+            }
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const int act = p.act;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
-                half4 h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = acc[a][b][4 * g + i] * alpha;
-                    h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
-                }
-                const u32x2 w = __builtin_bit_cast(u32x2, h);
-                const uint32_t elem = (uint32_t)m * (uint32_t)p.N + (uint32_t)n;
+                f32x4 bv;
                 if constexpr (VEC) {
-                    const uint32_t off = ((m < p.M) & (n < p.N)) ? elem * 2u : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                    bv = bias4(rbias, n);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t off = ((m < p.M) & (n + i < p.N)) ? (elem + i) * 2u : kOutOfRange;
-                        const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
-                        __builtin_amdgcn_raw_buffer_store_b16(hv, rc, off, 0, 0);
-                    }
+                    for (int i = 0; i < 4; ++i) bv[i] = (n + i < p.N) ? bias1(rbias, n + i) : 0.0f;
+                }
+#pragma unroll
+                for (int b = 0; b < TM; ++b) {
+                    const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+                    const f32x16 av = acc[a][b];
+                    f32x4 sv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                    store4(m, n, epilogue4(sv, alpha, bv, act));
                 }
             }
         }
     }
 }
 
-// K == 0: every output is the empty sum, i.e. +0.
-__global__ void __launch_bounds__(256) fill_zero_kernel(uint16_t* C, uint32_t count)
+// K == 0: every output is the empty sum, so C[m,n] = act(alpha * 0 + bias[n])
+// (+0 without a bias).
+__global__ void __launch_bounds__(256) fill_epilogue_kernel(uint16_t* C, uint32_t M, uint32_t N,
+                                                            const uint16_t* bias, float alpha, int act)
 {
+    const uint32_t count = M * N;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, count * 2u);
-    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < count; i += gridDim.x * 256u)
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rc, i * 2u, 0, 0);
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < count; i += gridDim.x * 256u) {
+        uint16_t out = 0;
+        if (bias != nullptr || act != kActRelu) {
+            const float b = bias ? (float)__builtin_bit_cast(_Float16, bias[i % N]) : 0.0f;
+            out = __builtin_bit_cast(uint16_t, (_Float16)activate(0.0f * alpha + b, act));
+        }
+        __builtin_amdgcn_raw_buffer_store_b16(out, rc, i * 2u, 0, 0);
+    }
 }
 
 }  // namespace gsr

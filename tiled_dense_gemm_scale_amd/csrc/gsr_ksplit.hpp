@@ -19,7 +19,8 @@
 //    publishes step t, and the MFMAs of step t-1 run behind them.
 //  * At the end the four partial tiles are summed through LDS in the MFMA
 //    lane layout (each 1 KiB write and read is contiguous), and each wave
-//    stores a quarter of the tile: scale, clamp at zero, round to fp16.
+//    stores a quarter of the tile: scale, clamp at zero, round to fp16 (or
+//    the epilogue variant: scale, bias, activation).
 #pragma once
 
 #include "gsr_pipeline.hpp"
@@ -236,6 +237,8 @@ gemm_scale_relu_ksplit_kernel(Problem p)
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
     const float alpha = p.alpha;
+    const bool plain = plain_epilogue(p);
+    const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
     // unit u = blk*4 + g goes to wave u % 4
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -252,10 +255,15 @@ gemm_scale_relu_ksplit_kernel(Problem p)
         const int m = m0 + b * 32 + (int)frow;
         const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
         half4 hv;
+        if (plain) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v = s[i] * alpha;
-            hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+            for (int i = 0; i < 4; ++i) {
+                const float v = s[i] * alpha;
+                hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+            }
+        } else {
+            const f32x4 sv = {s[0], s[1], s[2], s[3]};
+            hv = epilogue4(sv, alpha, bias4(rbias, n), p.act);
         }
         const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);

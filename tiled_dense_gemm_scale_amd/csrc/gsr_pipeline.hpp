@@ -294,22 +294,47 @@ gemm_scale_relu_pipe_kernel(Problem p)
 
     // ---- epilogue ------------------------------------------------------------
     const float alpha = p.alpha;
+    if (plain_epilogue(p)) {
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
-        for (int b = 0; b < TM; ++b) {
-            const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+            for (int b = 0; b < TM; ++b) {
+                const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
+                    half4 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = acc[a][b][4 * g + i] * alpha;
+                        h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                    }
+                    const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
+                }
+            }
+        }
+    } else {
+        // bias of the lane's four columns, then act(alpha * acc + bias)
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const int act = p.act;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
-                half4 h;
+                const f32x4 bv = bias4(rbias, n);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = acc[a][b][4 * g + i] * alpha;
-                    h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                for (int b = 0; b < TM; ++b) {
+                    const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+                    const f32x16 av = acc[a][b];
+                    f32x4 sv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                    const half4 h = epilogue4(sv, alpha, bv, act);
+                    const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
                 }
-                const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
             }
         }
     }

@@ -95,6 +95,17 @@ def integer_inputs(M: int, N: int, K: int, seed: int = 0, lo: int = -4, hi: int 
     return a.half(), b.half()
 
 
+def bias_input(N: int, seed: int = 0, std: float = 1.0, integer: bool = False) -> torch.Tensor:
+    """A bias vector (N,) fp16 CPU tensor for the epilogue variants: fp32
+    randn * std from its own CPU generator (seed + 1000003), narrowed to fp16;
+    or, with integer=True, integers uniform in [-4, 4]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 1000003)
+    if integer:
+        return torch.randint(-4, 5, (N,), generator=g, dtype=torch.int32).half()
+    return (torch.randn(N, generator=g, dtype=torch.float32) * std).half()
+
+
 def sample_points(M: int, N: int, count: int = 4096, seed: int = 1,
                   extra_rows: Optional[list] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Output coordinates to check on the largest shapes: the four corners,
