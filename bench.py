@@ -109,7 +109,13 @@ def capture(fn, stream, steps: int):
     return g
 
 
-def cpu_baseline(w, a, b, target_s: float):
+# --epilogue choices: (bias?, activation).  "relu" is the tutorial's operation
+# through gemm_scale_relu; the others go through gemm_scale_bias_act.
+EPILOGUES = {"relu": (False, "relu"), "bias-relu": (True, "relu"), "gelu": (False, "gelu"),
+             "bias-gelu": (True, "gelu"), "bias-none": (True, "none")}
+
+
+def cpu_baseline(w, a, b, target_s: float, epilogue: str = "relu", bias=None):
     """The oracle, as it is, on a bounded sample of the same workload: the
     first R rows of A against all of B, R sized for about `target_s` seconds."""
     from oracle import oracle
@@ -119,16 +125,25 @@ def cpu_baseline(w, a, b, target_s: float):
     threads = oracle.default_threads()
     a_bits = W.fp16_bits(a)
     b_bits = W.fp16_bits(b)
+    act = {"relu": oracle.ACT_RELU, "gelu": oracle.ACT_GELU, "none": oracle.ACT_NONE}[EPILOGUES[epilogue][1]]
+    bias_bits = W.fp16_bits(bias) if bias is not None else None
+
+    def run(rows):
+        if epilogue == "relu":
+            orc.gemm_scale_relu(a_bits[:rows], b_bits, w.alpha, nthreads=threads)
+        else:
+            orc.gemm_bias_act(a_bits[:rows], b_bits, bias_bits, w.alpha, act, nthreads=threads)
+
     # calibrate on a few rows, then size the sample
     rows = min(w.M, max(threads, 8))
     t0 = time.perf_counter()
-    orc.gemm_scale_relu(a_bits[:rows], b_bits, w.alpha, nthreads=threads)
+    run(rows)
     t_cal = time.perf_counter() - t0
     per_row = t_cal / rows
     R = int(min(w.M, max(rows, target_s / max(per_row, 1e-9))))
     R = max(threads, (R // threads) * threads) if R < w.M else w.M
     t0 = time.perf_counter()
-    orc.gemm_scale_relu(a_bits[:R], b_bits, w.alpha, nthreads=threads)
+    run(R)
     t = time.perf_counter() - t0
     flops = 2.0 * R * w.N * w.K
     return {
@@ -148,6 +163,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--config-id", type=int, default=-1, help="force a tile configuration")
+    ap.add_argument("--epilogue", choices=sorted(EPILOGUES), default="relu",
+                    help="relu: the tutorial's C = ReLU(alpha A B); the others time the epilogue variants "
+                         "C = act(alpha A B + bias) (bias: seeded N(0,1) fp16 per column)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--repeats", type=int, default=5,
@@ -192,8 +210,15 @@ def main(argv=None) -> int:
     cfg = gsr.select_config(w.M, w.N, w.K) if args.config_id < 0 else gsr.get_config(args.config_id)
     log(f"[bench] tile config {cfg}")
 
+    has_bias, act = EPILOGUES[args.epilogue]
+    bias_cpu = W.bias_input(w.N) if has_bias else None
+    bias = bias_cpu.to(dev) if has_bias else None
+
     def step():
-        gsr.gemm_scale_relu_ex(a, b, w.alpha, args.config_id, c=c, stream=stream)
+        if args.epilogue == "relu":
+            gsr.gemm_scale_relu_ex(a, b, w.alpha, args.config_id, c=c, stream=stream)
+        else:
+            gsr.gemm_scale_bias_act(a, b, bias, w.alpha, act, c=c, stream=stream, config_id=args.config_id)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -248,8 +273,8 @@ def main(argv=None) -> int:
         za = torch.zeros_like(a)
         zb = torch.zeros_like(b)
         zc = torch.empty_like(c)
-        gz = capture(lambda: gsr.gemm_scale_relu_ex(za, zb, w.alpha, args.config_id, c=zc, stream=stream),
-                     stream, args.steps)
+        gz = capture(lambda: gsr.gemm_scale_bias_act(za, zb, bias, w.alpha, act, c=zc, stream=stream,
+                                                     config_id=args.config_id), stream, args.steps)
         zms = min(time_graph(gz, stream, args.steps, 1))
         context["zero_input_tflops"] = round(w.flops / (zms * 1e-3) / 1e12, 3)
         del gz, za, zb, zc
@@ -284,7 +309,7 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)")
-        cpu = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds)
+        cpu = cpu_baseline(w, a_cpu, b_cpu, args.cpu_seconds, args.epilogue, bias_cpu)
         log(f"[bench] cpu_baseline {cpu}")
 
     out = {
@@ -305,6 +330,7 @@ def main(argv=None) -> int:
             "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
             "inputs": f"seed 0 randn fp32 -> fp16, A then B, B std {w.b_std:g}",
             "launch": args.launch,
+            "epilogue": args.epilogue,
             "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n")},
             "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),

@@ -310,6 +310,20 @@ gemm_scale_relu_ilv_kernel(Problem p)
     // segments (16 lanes per row) instead of 16 bytes in each of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at
     // physical chunk c ^ (r % 16).
     static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
+    // The variant's bias values for the lane's 16 column groups are requested
+    // before the barrier, so their latency overlaps it.
+    const bool plain = plain_epilogue(p);
+    f32x4 bvs[TN][4];
+    {
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const bool load = !plain && p.bias != nullptr;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bvs[a][g] = load ? bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi)
+                                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     lds_barrier();  // every wave is past its last operand read
     const float alpha = p.alpha;
     uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
@@ -318,7 +332,7 @@ gemm_scale_relu_ilv_kernel(Problem p)
         const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
         *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
     };
-    if (plain_epilogue(p)) {
+    if (plain) {
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
 #pragma unroll
@@ -336,24 +350,25 @@ gemm_scale_relu_ilv_kernel(Problem p)
             }
         }
     } else {
-        // bias of the lane's four columns, then act(alpha * acc + bias)
-        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const int act = p.act;
+        // act(alpha * acc + bias)
+        with_activation(p.act, [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-        for (int a = 0; a < TN; ++a) {
+            for (int a = 0; a < TN; ++a) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 bv = bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi);
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 bv = bvs[a][g];
 #pragma unroll
-                for (int b = 0; b < TM; ++b) {
-                    const f32x16 av = acc[a][b];
-                    f32x4 sv;
+                    for (int b = 0; b < TM; ++b) {
+                        const f32x16 av = acc[a][b];
+                        f32x4 sv;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
-                    stage4(a, b, g, epilogue4(sv, alpha, bv, act));
+                        for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                        stage4(a, b, g, epilogue4<ACT>(sv, alpha, bv));
+                    }
                 }
             }
-        }
+        });
     }
     // The reads below take what other lanes of this wave wrote: LDS keeps a
     // wave's accesses in order, so only the compiler must not move them.

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gsr {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -117,12 +119,16 @@ struct Problem {
 enum : int { kActRelu = 0, kActGelu = 1, kActNone = 2 };
 
 // GELU, tanh form: y/2 (1 + tanh(u)) = y / (1 + exp(-2u)) with
-// u = sqrt(2/pi) (y + 0.044715 y^3).  exp(-2u) overflowing to +inf (very
-// negative y) gives -0, underflowing to 0 (large y) gives y.
+// u = sqrt(2/pi) (y + 0.044715 y^3), evaluated with the hardware base-2
+// exponential and reciprocal (about 1 ulp each, far below the fp16 output
+// rounding).  exp(-2u) overflowing to +inf (very negative y) gives -0,
+// underflowing to 0 (large y) gives y.
 __device__ __forceinline__ float gelu_tanh(float y)
 {
-    const float u = 0.7978845608028654f * (y + 0.044715f * (y * y * y));
-    return y / (1.0f + __expf(-2.0f * u));
+    // -2 * sqrt(2/pi) * log2(e), so that exp(-2u) = 2^(t * (y + 0.044715 y^3))
+    constexpr float t = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    const float e = __builtin_amdgcn_exp2f(t * (y + 0.044715f * (y * y * y)));
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 __device__ __forceinline__ float activate(float y, int act)
@@ -162,13 +168,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const Problem& p)
                                              p.bias ? p.N * 2 : 0, 0x00020000);
 }
 
+// The activation as a compile-time choice, so an epilogue loop carries no
+// per-element branch.
+template <int ACT>
+__device__ __forceinline__ float activate_t(float y)
+{
+    if constexpr (ACT == kActRelu) return y > 0.0f ? y : 0.0f;
+    else if constexpr (ACT == kActGelu) return gelu_tanh(y);
+    else return y;
+}
+
 // act(alpha * s + b) for four outputs, narrowed to fp16 (round to nearest even).
-__device__ __forceinline__ half4 epilogue4(f32x4 s, float alpha, f32x4 b, int act)
+template <int ACT>
+__device__ __forceinline__ half4 epilogue4(f32x4 s, float alpha, f32x4 b)
 {
     half4 h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = (_Float16)activate(s[i] * alpha + b[i], act);
+    for (int i = 0; i < 4; ++i) h[i] = (_Float16)activate_t<ACT>(s[i] * alpha + b[i]);
     return h;
+}
+
+// Runs f(std::integral_constant<int, ACT>) for the run-time activation code:
+// one uniform branch per epilogue instead of one per element.
+template <class F>
+__device__ __forceinline__ void with_activation(int act, F&& f)
+{
+    if (act == kActGelu) f(std::integral_constant<int, kActGelu>{});
+    else if (act == kActNone) f(std::integral_constant<int, kActNone>{});
+    else f(std::integral_constant<int, kActRelu>{});
 }
 
 // Workgroup id -> (tile row, tile column).
@@ -402,31 +429,44 @@ gemm_scale_relu_kernel(Problem p)
             }
         }
     } else {
+        // the bias of the lane's columns, all requested before the first use
         const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const int act = p.act;
+        f32x4 bvs[TN][4];
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
-                f32x4 bv;
-                if constexpr (VEC) {
-                    bv = bias4(rbias, n);
+                if (p.bias == nullptr) {
+                    bvs[a][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                } else if constexpr (VEC) {
+                    bvs[a][g] = bias4(rbias, n);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bv[i] = (n + i < p.N) ? bias1(rbias, n + i) : 0.0f;
-                }
-#pragma unroll
-                for (int b = 0; b < TM; ++b) {
-                    const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
-                    const f32x16 av = acc[a][b];
-                    f32x4 sv;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
-                    store4(m, n, epilogue4(sv, alpha, bv, act));
+                    for (int i = 0; i < 4; ++i) bvs[a][g][i] = (n + i < p.N) ? bias1(rbias, n + i) : 0.0f;
                 }
             }
         }
+        with_activation(p.act, [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
+                    const f32x4 bv = bvs[a][g];
+#pragma unroll
+                    for (int b = 0; b < TM; ++b) {
+                        const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+                        const f32x16 av = acc[a][b];
+                        f32x4 sv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                        store4(m, n, epilogue4<ACT>(sv, alpha, bv));
+                    }
+                }
+            }
+        });
     }
 }
 

@@ -215,6 +215,21 @@ gemm_scale_relu_ksplit_kernel(Problem p)
     }
 
     // ---- sum the four partial tiles through LDS ---------------------------------
+    // The variant's bias values of this wave's output units are requested
+    // first, so their latency overlaps the reduction.
+    const bool plain = plain_epilogue(p);
+    f32x4 bvs[NB];
+    {
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const bool load = !plain && p.bias != nullptr;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int u = j * NW + wave;
+            const int blk = u >> 2, g = u & 3;
+            const int n = n0 + (blk / TM) * 32 + 8 * g + 4 * (int)fhi;
+            bvs[j] = load ? bias4(rbias, n) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
     wait_vmcnt<0>();
     lds_barrier();  // every wave is done with the operand buffers
     // slot (w, blk, g): 64 lanes x 16 bytes, lane-contiguous
@@ -237,37 +252,38 @@ gemm_scale_relu_ksplit_kernel(Problem p)
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
     const float alpha = p.alpha;
-    const bool plain = plain_epilogue(p);
-    const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
     // unit u = blk*4 + g goes to wave u % 4
+    with_activation(p.act, [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int u = j * NW + wave;
-        const int blk = u >> 2, g = u & 3;
-        const int a = blk / TM, b = blk % TM;
-        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NB; ++j) {
+            const int u = j * NW + wave;
+            const int blk = u >> 2, g = u & 3;
+            const int a = blk / TM, b = blk % TM;
+            float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const f32x4 v = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
+            for (int w = 0; w < NW; ++w) {
+                const f32x4 v = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] += v[i];
-        }
-        const int m = m0 + b * 32 + (int)frow;
-        const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
-        half4 hv;
-        if (plain) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = s[i] * alpha;
-                hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                for (int i = 0; i < 4; ++i) s[i] += v[i];
             }
-        } else {
-            const f32x4 sv = {s[0], s[1], s[2], s[3]};
-            hv = epilogue4(sv, alpha, bias4(rbias, n), p.act);
+            const int m = m0 + b * 32 + (int)frow;
+            const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
+            half4 hv;
+            if (plain) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = s[i] * alpha;
+                    hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                }
+            } else {
+                const f32x4 sv = {s[0], s[1], s[2], s[3]};
+                hv = epilogue4<ACT>(sv, alpha, bvs[j]);
+            }
+            const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);
         }
-        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);
-    }
+    });
 }
 
 }  // namespace gsr

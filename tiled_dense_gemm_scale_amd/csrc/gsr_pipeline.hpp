@@ -315,28 +315,38 @@ gemm_scale_relu_pipe_kernel(Problem p)
             }
         }
     } else {
-        // bias of the lane's four columns, then act(alpha * acc + bias)
+        // bias of the lane's columns (all requested before the first use),
+        // then act(alpha * acc + bias)
         const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const int act = p.act;
+        f32x4 bvs[TN][4];
 #pragma unroll
-        for (int a = 0; a < TN; ++a) {
+        for (int a = 0; a < TN; ++a)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
-                const f32x4 bv = bias4(rbias, n);
+            for (int g = 0; g < 4; ++g)
+                bvs[a][g] = p.bias ? bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi)
+                                   : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        with_activation(p.act, [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-                for (int b = 0; b < TM; ++b) {
-                    const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
-                    const f32x16 av = acc[a][b];
-                    f32x4 sv;
+            for (int a = 0; a < TN; ++a) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
-                    const half4 h = epilogue4(sv, alpha, bv, act);
-                    const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi;
+                    const f32x4 bv = bvs[a][g];
+#pragma unroll
+                    for (int b = 0; b < TM; ++b) {
+                        const int m = m0 + wm * T::WTM + b * 32 + (int)frow;
+                        const f32x16 av = acc[a][b];
+                        f32x4 sv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                        const half4 h = epilogue4<ACT>(sv, alpha, bv);
+                        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rc, off, 0, 0);
+                    }
                 }
             }
-        }
+        });
     }
 }
 
