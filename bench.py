@@ -171,6 +171,8 @@ def main(argv=None) -> int:
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra replays of the timed graph for median/min (graph launch only)")
     ap.add_argument("--no-context", action="store_true", help="skip the dispatch-floor measurement")
+    ap.add_argument("--no-torch-context", action="store_true",
+                    help="skip timing torch's unfused matmul -> mul -> relu and its plain fp16 matmul")
     ap.add_argument("--zero-input", action="store_true",
                     help="also time the same kernel on all-zero inputs (runs the timed kernel again, "
                          "so leave it off when profiling per-kernel averages)")
@@ -269,6 +271,28 @@ def main(argv=None) -> int:
         context["dispatch_floor_us"] = round(floor * 1e3, 3)
         del g0
         log(f"[bench] dispatch floor {context['dispatch_floor_us']} us/launch")
+    if graph is not None and not args.no_torch_context and args.epilogue == "relu":
+        # The tutorial's comparison: its fused kernel against torch's
+        # relu((a @ b) * scale), three kernels with two fp16 round trips of C
+        # through HBM; and torch's fp16 matmul alone (the vendor GEMM, no
+        # epilogue).  Context only: another library, timed the same way.
+        alpha = w.alpha
+        with torch.cuda.stream(stream):  # the vendor GEMM sets itself up on first use, outside capture
+            for _ in range(3):
+                torch.relu(torch.matmul(a, b) * alpha)
+        torch.cuda.synchronize()
+        gu = capture(lambda: torch.relu(torch.matmul(a, b) * alpha), stream, args.steps)
+        tu = min(time_graph(gu, stream, args.steps, 2))
+        del gu
+        gm = capture(lambda: torch.matmul(a, b), stream, args.steps)
+        tm = min(time_graph(gm, stream, args.steps, 2))
+        del gm
+        torch.cuda.empty_cache()
+        context["torch_unfused_tflops"] = round(w.flops / (tu * 1e-3) / 1e12, 3)
+        context["torch_matmul_only_tflops"] = round(w.flops / (tm * 1e-3) / 1e12, 3)
+        context["speedup_vs_torch_unfused"] = round(tu / ms, 3)
+        log(f"[bench] torch unfused {tu * 1e3:.2f} us ({context['torch_unfused_tflops']} TFLOP/s), "
+            f"torch matmul only {tm * 1e3:.2f} us ({context['torch_matmul_only_tflops']} TFLOP/s)")
     if graph is not None and args.zero_input:
         za = torch.zeros_like(a)
         zb = torch.zeros_like(b)
