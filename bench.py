@@ -166,6 +166,9 @@ def main(argv=None) -> int:
     ap.add_argument("--epilogue", choices=sorted(EPILOGUES), default="relu",
                     help="relu: the tutorial's C = ReLU(alpha A B); the others time the epilogue variants "
                          "C = act(alpha A B + bias) (bias: seeded N(0,1) fp16 per column)")
+    ap.add_argument("--tuning", default=None,
+                    help="load a tuning table (gsr_load_tuning format, e.g. written by "
+                         "python -m tiled_dense_gemm_scale_amd.tune) before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--repeats", type=int, default=5,
@@ -209,6 +212,9 @@ def main(argv=None) -> int:
     c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     stream = torch.cuda.Stream(dev)
     torch.cuda.synchronize()
+    if args.tuning:
+        gsr.load_tuning(args.tuning)
+        log(f"[bench] tuning table {args.tuning}: {gsr.tuning_entries()} entries")
     cfg = gsr.select_config(w.M, w.N, w.K) if args.config_id < 0 else gsr.get_config(args.config_id)
     log(f"[bench] tile config {cfg}")
 
@@ -355,7 +361,9 @@ def main(argv=None) -> int:
             "inputs": f"seed 0 randn fp32 -> fp16, A then B, B std {w.b_std:g}",
             "launch": args.launch,
             "epilogue": args.epilogue,
-            "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n")},
+            "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n", "group_m",
+                                         "xcd_remap")},
+            "tuning": os.path.relpath(args.tuning, ROOT) if args.tuning else None,
             "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
             "device": {"cus": dinfo.get("cus"), "max_clock_mhz": (dinfo["clock_khz"] / 1000.0) if "clock_khz" in dinfo else None},

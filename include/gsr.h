@@ -116,7 +116,35 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K,
                            const void* A, const void* B, const void* bias, void* C,
                            float alpha, int32_t activation, void* stream, int32_t config_id);
 
-/* The configuration the selector picks for an M x N x K problem.  Host only;
+/* As gemm_scale_bias_act with an explicit launch: cfg->id picks the compiled
+ * tile configuration; cfg->group_m (1..4096, tile rows per group of the
+ * launch order) and cfg->xcd_remap (0 or 1) override that configuration's
+ * launch order; the other fields are ignored.  The launch order changes only
+ * which tiles run together, never a tile's arithmetic, so results are bit
+ * for bit those of gemm_scale_bias_act_ex with the same id.  For tuning
+ * sweeps.  GSR_ERROR_INVALID_CONFIG for an out-of-range field. */
+int gemm_scale_bias_act_cfg(int64_t M, int64_t N, int64_t K,
+                            const void* A, const void* B, const void* bias, void* C,
+                            float alpha, int32_t activation, void* stream, const gsr_config* cfg);
+
+/* Tuning table: exact problem shapes mapped to a launch, consulted before the
+ * built-in selector (by every entry point called with config id -1, and by
+ * gsr_select_config).  The file is text, one entry per line,
+ *     M N K config_id group_m xcd_remap
+ * with '#' starting a comment; tiled_dense_gemm_scale_amd/tune.py writes it
+ * from measured sweeps (the aikraft.ru TileLang guide: section 3, a manual
+ * sweep of tile, stage and swizzle knobs that finds no schedule best for
+ * every size; section 7, an automatic search of that space per problem and
+ * GPU).  gsr_load_tuning replaces the table, or returns
+ * GSR_ERROR_INVALID_VALUE for an unreadable or malformed file and keeps the
+ * previous one; gsr_clear_tuning empties it; gsr_tuning_entries counts it.
+ * Host only, thread-safe. */
+int gsr_load_tuning(const char* path);
+int gsr_clear_tuning(void);
+int gsr_tuning_entries(void);
+
+/* The configuration the selector picks for an M x N x K problem (the tuning
+ * table first, with its launch order in group_m / xcd_remap).  Host only;
  * touches no device.  Returns GSR_SUCCESS or GSR_ERROR_INVALID_VALUE. */
 int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out);
 

@@ -147,3 +147,47 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_native, "LIBRARY", "/nonexistent/libgsr.so")
     with pytest.raises(RuntimeError, match="not built"):
         _native.lib()
+
+
+def test_tuning_table_host_side(native, tmp_path):
+    """The tuning table is parsed and consulted on the host: select_config
+    reports the tuned launch for an exact shape and the built-in choice
+    otherwise; a malformed file is rejected and the previous table kept."""
+    native.clear_tuning()
+    base = native.select_config(1024, 1024, 1024)
+    other = native.select_config(1024, 1024, 1025)
+    good = tmp_path / "t.txt"
+    good.write_text("# comment line\n\n1024 1024 1024 7 2 0   # trailing comment\n300 520 200 15 8 1\n")
+    native.load_tuning(str(good))
+    try:
+        assert native.tuning_entries() == 2
+        c = native.select_config(1024, 1024, 1024)
+        assert (c["id"], c["group_m"], c["xcd_remap"]) == (7, 2, 0)
+        c = native.select_config(300, 520, 200)
+        assert (c["id"], c["group_m"], c["xcd_remap"]) == (15, 8, 1)
+        assert native.select_config(1024, 1024, 1025) == other  # not in the table
+        for bad in ("1024 1024 1024 99 1 0\n",      # unknown config id
+                    "1024 1024 1024 7 0 0\n",       # group_m < 1
+                    "1024 1024 1024 7 1 2\n",       # xcd_remap not 0/1
+                    "1024 1024 7 1 0\n",            # too few fields
+                    "1024 1024 1024 7 1 0 5\n",     # too many fields
+                    "-1 4 4 7 1 0\n",               # negative size
+                    "hello\n"):
+            p = tmp_path / "bad.txt"
+            p.write_text(bad)
+            with pytest.raises(native.GsrError):
+                native.load_tuning(str(p))
+            assert native.tuning_entries() == 2  # previous table kept
+        with pytest.raises(native.GsrError):
+            native.load_tuning(str(tmp_path / "missing.txt"))
+    finally:
+        native.clear_tuning()
+    assert native.tuning_entries() == 0
+    assert native.select_config(1024, 1024, 1024) == base
+
+
+def test_launch_entry_point_checks(native):
+    # explicit launches are validated on the host before any device work
+    for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (7, 0, 1), (7, 5000, 1), (7, 4, 2)):
+        st = native.gemm_scale_bias_act_cfg(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 0, 0, cid, gm, xcd)
+        assert st == 6, (cid, gm, xcd, st)

@@ -24,10 +24,12 @@ from typing import Optional
 import torch
 
 from . import _native
-from ._native import GsrError, get_config, num_configs, select_config, status_string, version
+from ._native import (GsrError, clear_tuning, get_config, load_tuning, num_configs, select_config, status_string,
+                      tuning_entries, version)
 
-__all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "GsrError", "select_config",
-           "get_config", "num_configs", "status_string", "version", "configs", "ACTIVATIONS"]
+__all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "gemm_launch", "GsrError",
+           "select_config", "get_config", "num_configs", "status_string", "version", "configs", "ACTIVATIONS",
+           "load_tuning", "clear_tuning", "tuning_entries"]
 
 ACTIVATIONS = {"relu": _native.GSR_ACT_RELU, "gelu": _native.GSR_ACT_GELU, "none": _native.GSR_ACT_NONE}
 
@@ -99,6 +101,27 @@ def gemm_scale_bias_act(a: torch.Tensor, b: torch.Tensor, bias: Optional[torch.T
         s = _stream_handle(a.device, stream)
         st = _native.gemm_scale_bias_act(M, N, K, a.data_ptr(), b.data_ptr(), bptr, c.data_ptr(), alpha,
                                          ACTIVATIONS[activation], s, config_id)
+    _native.check(st)
+    return c
+
+
+def gemm_launch(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id: int, group_m: int, xcd_remap: int,
+                bias: Optional[torch.Tensor] = None, activation: str = "relu", c: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """act(alpha * a @ b + bias) with an explicit launch: tile configuration,
+    tile rows per launch group and XCD regrouping (tuning sweeps)."""
+    M, N, K, c = _check_operands(a, b, c)
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
+    bptr = 0
+    if bias is not None:
+        if bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous():
+            raise ValueError(f"bias must be a contiguous ({N},) float16 device tensor")
+        bptr = bias.data_ptr()
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_bias_act_cfg(M, N, K, a.data_ptr(), b.data_ptr(), bptr, c.data_ptr(), alpha,
+                                             ACTIVATIONS[activation], s, config_id, group_m, xcd_remap)
     _native.check(st)
     return c
 

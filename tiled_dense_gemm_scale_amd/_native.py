@@ -75,6 +75,15 @@ def lib() -> ctypes.CDLL:
             L.gemm_scale_bias_act.restype = ctypes.c_int
             L.gemm_scale_bias_act_ex.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, i32]
             L.gemm_scale_bias_act_ex.restype = ctypes.c_int
+            L.gemm_scale_bias_act_cfg.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp,
+                                                   ctypes.POINTER(GsrConfig)]
+            L.gemm_scale_bias_act_cfg.restype = ctypes.c_int
+            L.gsr_load_tuning.argtypes = [ctypes.c_char_p]
+            L.gsr_load_tuning.restype = ctypes.c_int
+            L.gsr_clear_tuning.argtypes = []
+            L.gsr_clear_tuning.restype = ctypes.c_int
+            L.gsr_tuning_entries.argtypes = []
+            L.gsr_tuning_entries.restype = ctypes.c_int
             L.gsr_select_config.argtypes = [i64, i64, i64, ctypes.POINTER(GsrConfig)]
             L.gsr_select_config.restype = ctypes.c_int
             L.gsr_num_configs.argtypes = []
@@ -116,6 +125,29 @@ def gemm_scale_bias_act(M: int, N: int, K: int, A: int, B: int, bias: int, C: in
     gsr_status."""
     return lib().gemm_scale_bias_act_ex(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
                                         int(activation), stream or None, int(config_id))
+
+
+def gemm_scale_bias_act_cfg(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, alpha: float,
+                            activation: int, stream: int, config_id: int, group_m: int, xcd_remap: int) -> int:
+    """Raw entry point with an explicit launch (tile config id, group_m,
+    xcd_remap).  Returns the gsr_status."""
+    cfg = GsrConfig()
+    cfg.id, cfg.group_m, cfg.xcd_remap = int(config_id), int(group_m), int(xcd_remap)
+    return lib().gemm_scale_bias_act_cfg(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
+                                         int(activation), stream or None, ctypes.byref(cfg))
+
+
+def load_tuning(path: str) -> None:
+    """Load a tuning table (text: "M N K config_id group_m xcd_remap" per line)."""
+    check(lib().gsr_load_tuning(os.fsencode(path)))
+
+
+def clear_tuning() -> None:
+    check(lib().gsr_clear_tuning())
+
+
+def tuning_entries() -> int:
+    return int(lib().gsr_tuning_entries())
 
 
 def select_config(M: int, N: int, K: int) -> dict:

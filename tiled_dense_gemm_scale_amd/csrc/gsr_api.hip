@@ -2,10 +2,13 @@
 // checks, device check, tile selection and the launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "gsr.h"
 #include "gsr_kernels.hpp"
@@ -167,6 +170,40 @@ int select(int64_t M, int64_t N, int64_t K)
     return best;
 }
 
+// ---- tuning table: exact shapes -> launch choice ---------------------------
+// Written by an offline sweep (tiled_dense_gemm_scale_amd/tune.py) and loaded
+// with gsr_load_tuning; a shape found here overrides select().
+struct Launch {
+    int id, group_m, xcd_remap;
+};
+struct Tuned {
+    int64_t M, N, K;
+    Launch l;
+};
+std::mutex g_tune_mu;
+std::vector<Tuned> g_tuned;
+std::atomic<bool> g_have_tuning{false};
+
+bool valid_launch(const Launch& l)
+{
+    return l.id >= 0 && l.id < kNumConfigs && l.group_m >= 1 && l.group_m <= 4096 &&
+           (l.xcd_remap == 0 || l.xcd_remap == 1);
+}
+
+// The launch for a problem: a forced config id keeps its compiled launch
+// order; otherwise the tuning table, else the selector.
+Launch resolve(int64_t M, int64_t N, int64_t K, int config_id)
+{
+    if (config_id >= 0) return Launch{config_id, kTable[config_id].cfg.group_m, kTable[config_id].cfg.xcd_remap};
+    if (g_have_tuning.load(std::memory_order_acquire)) {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        for (const Tuned& t : g_tuned)
+            if (t.M == M && t.N == N && t.K == K) return t.l;
+    }
+    const int id = select(M, N, K);
+    return Launch{id, kTable[id].cfg.group_m, kTable[id].cfg.xcd_remap};
+}
+
 struct DeviceInfo {
     bool ok;
     bool gfx950;
@@ -261,12 +298,21 @@ int gsr_get_config(int32_t config_id, gsr_config* out)
 int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out)
 {
     if (out == nullptr || M < 0 || N < 0 || K < 0) return GSR_ERROR_INVALID_VALUE;
-    *out = kTable[select(M, N, K)].cfg;
+    const Launch l = resolve(M, N, K, -1);
+    *out = kTable[l.id].cfg;
+    out->group_m = l.group_m;
+    out->xcd_remap = l.xcd_remap;
     return GSR_SUCCESS;
 }
 
-int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
-                           void* C, float alpha, int32_t activation, void* stream, int32_t config_id)
+}  // extern "C"
+
+namespace {
+
+// Checks, then the launch.  `forced` >= 0 is a config id, -1 the selector,
+// -2 the launch in `given`.
+int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, float alpha,
+        int32_t activation, void* stream, int forced, const Launch& given)
 {
     int st = validate(M, N, K, A, B, C);
     if (st != GSR_SUCCESS) return st;
@@ -278,7 +324,8 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const
         if ((uintptr_t)bias & 1u) return GSR_ERROR_INVALID_VALUE;
         if (overlaps(bias, (uint64_t)N * 2u, C, (uint64_t)M * (uint64_t)N * 2u)) return GSR_ERROR_INVALID_VALUE;
     }
-    if (config_id < -1 || config_id >= kNumConfigs) return GSR_ERROR_INVALID_CONFIG;
+    if (forced < -2 || forced >= kNumConfigs) return GSR_ERROR_INVALID_CONFIG;
+    if (forced == -2 && !valid_launch(given)) return GSR_ERROR_INVALID_CONFIG;
     if (M == 0 || N == 0) return GSR_SUCCESS;
     st = check_device();
     if (st != GSR_SUCCESS) return st;
@@ -292,7 +339,8 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const
         return hipGetLastError() == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
     }
 
-    const Entry& e = kTable[config_id < 0 ? select(M, N, K) : config_id];
+    const Launch l = (forced == -2) ? given : resolve(M, N, K, forced);
+    const Entry& e = kTable[l.id];
     Problem p;
     p.A = (const uint16_t*)A;
     p.B = (const uint16_t*)B;
@@ -305,14 +353,84 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const
     p.act = (int)activation;
     p.tiles_m = (int)cdiv(M, e.cfg.block_m);
     p.tiles_n = (int)cdiv(N, e.cfg.block_n);
-    p.group_m = e.cfg.group_m;
-    p.xcd_remap = e.cfg.xcd_remap;
+    p.group_m = l.group_m;
+    p.xcd_remap = l.xcd_remap;
     const int grid = p.tiles_m * p.tiles_n;
     const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
                      (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 7u) == 0) &&
                      (((uintptr_t)bias & 7u) == 0);
     const hipError_t err = (vec ? e.vec : e.elem)(p, grid, s);
     return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                           void* C, float alpha, int32_t activation, void* stream, int32_t config_id)
+{
+    if (config_id < -1) return GSR_ERROR_INVALID_CONFIG;
+    return run(M, N, K, A, B, bias, C, alpha, activation, stream, config_id, Launch{0, 0, 0});
+}
+
+int gemm_scale_bias_act_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                            void* C, float alpha, int32_t activation, void* stream, const gsr_config* cfg)
+{
+    if (cfg == nullptr) return GSR_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, B, bias, C, alpha, activation, stream, -2, Launch{cfg->id, cfg->group_m, cfg->xcd_remap});
+}
+
+int gsr_load_tuning(const char* path)
+{
+    if (path == nullptr) return GSR_ERROR_INVALID_VALUE;
+    FILE* f = std::fopen(path, "r");
+    if (f == nullptr) return GSR_ERROR_INVALID_VALUE;
+    std::vector<Tuned> table;
+    char line[512];
+    int st = GSR_SUCCESS;
+    while (std::fgets(line, sizeof line, f) != nullptr) {
+        char* hash = std::strchr(line, '#');
+        if (hash != nullptr) *hash = 0;
+        long long m, n, k;
+        int id, gm, xr;
+        char extra;
+        const int got = std::sscanf(line, "%lld %lld %lld %d %d %d %c", &m, &n, &k, &id, &gm, &xr, &extra);
+        if (got <= 0) {  // blank or comment line
+            bool blank = true;
+            for (const char* c = line; *c; ++c)
+                if (*c != ' ' && *c != '\t' && *c != '\n' && *c != '\r') blank = false;
+            if (blank) continue;
+            st = GSR_ERROR_INVALID_VALUE;
+            break;
+        }
+        const Tuned t{m, n, k, Launch{id, gm, xr}};
+        if (got != 6 || m < 0 || n < 0 || k < 0 || !valid_launch(t.l)) {
+            st = GSR_ERROR_INVALID_VALUE;
+            break;
+        }
+        table.push_back(t);
+    }
+    std::fclose(f);
+    if (st != GSR_SUCCESS) return st;  // the previous table stays
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.swap(table);
+    g_have_tuning.store(!g_tuned.empty(), std::memory_order_release);
+    return GSR_SUCCESS;
+}
+
+int gsr_clear_tuning(void)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.clear();
+    g_have_tuning.store(false, std::memory_order_release);
+    return GSR_SUCCESS;
+}
+
+int gsr_tuning_entries(void)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return (int)g_tuned.size();
 }
 
 int gemm_scale_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,

@@ -1,0 +1,217 @@
+"""Offline autotuner for the tile selector.
+
+The aikraft.ru TileLang guide sweeps tile, stage and swizzle knobs by hand
+and finds no schedule best for every size (section 3), then searches that
+space automatically per problem and GPU (section 7).  Here the space is the
+library's compiled tile configurations and, for each, its launch order (tile
+rows per launch group, XCD regrouping).  For every problem shape:
+
+  1. every compiled configuration is timed with its own launch order;
+  2. the three fastest are timed again with group_m in {1, 2, 4, 8, 16} and
+     XCD regrouping on and off;
+  3. each candidate's output is checked against the built-in selector's
+     (tolerance 1e-2 + 1e-2 |ref|: different tiles sum in different orders),
+     and launch-order variants of one configuration must match it bit for bit;
+  4. the fastest valid candidate is kept if it beats the selector by more
+     than --min-gain (default 1 %, about the run-to-run spread), else the
+     selector's own launch is written.
+
+Timing: each candidate is captured as a HIP graph of `steps` calls and
+replayed twice, timed with events on the launch stream; the faster replay
+counts.  Output: a tuning table for gsr_load_tuning (text, one
+"M N K config_id group_m xcd_remap" line per shape) and a JSON report with
+every timing, the speedup over the built-in selector and the Pareto set of
+(time, LDS bytes per workgroup).
+
+Usage:
+  python -m tiled_dense_gemm_scale_amd.tune --shapes square_1024,4096x4096x4096 \\
+      --out tuning.txt --report tuning.json
+Shapes are MxNxK or the names of the benchmark workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+from typing import Dict, List, Tuple
+
+import torch
+
+from . import workloads as W
+
+GROUPS = (1, 2, 4, 8, 16)
+
+
+def parse_shape(text: str) -> Tuple[str, int, int, int, float, float]:
+    """(name, M, N, K, alpha, b_std) for a workload name or MxNxK."""
+    if text in W.WORKLOADS:
+        w = W.WORKLOADS[text]
+        return w.name, w.M, w.N, w.K, w.alpha, w.b_std
+    if text == W.SKINNY.name:
+        w = W.SKINNY
+        return w.name, w.M, w.N, w.K, w.alpha, w.b_std
+    m, n, k = (int(v) for v in text.lower().split("x"))
+    return text, m, n, k, 0.5, 1.0
+
+
+def time_calls(fn, stream, steps: int) -> float:
+    """Microseconds per call: `steps` calls captured once, replayed twice."""
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            fn()
+    best = float("inf")
+    for _ in range(2):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / steps)
+    del g
+    return best
+
+
+def close(x: torch.Tensor, ref: torch.Tensor) -> bool:
+    xf, rf = x.float(), ref.float()
+    return bool(torch.all(torch.abs(xf - rf) <= 1e-2 + 1e-2 * torch.abs(rf)).item())
+
+
+def pareto(cands: List[dict]) -> List[dict]:
+    """Candidates not beaten on both time and LDS bytes by another."""
+    out = []
+    for c in cands:
+        dominated = any(o["us"] <= c["us"] and o["lds_bytes"] <= c["lds_bytes"]
+                        and (o["us"] < c["us"] or o["lds_bytes"] < c["lds_bytes"]) for o in cands)
+        if not dominated:
+            out.append(c)
+    return sorted(out, key=lambda c: c["us"])
+
+
+def tune_shape(gsr, text: str, top: int, min_gain: float, log) -> Dict:
+    name, M, N, K, alpha, b_std = parse_shape(text)
+    dev = torch.device("cuda:0")
+    a, b = W.normal_inputs(M, N, K, seed=0, b_std=b_std)
+    a, b = a.to(dev), b.to(dev)
+    c = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream(dev)
+    flops = 2.0 * M * N * K
+    steps = int(min(200, max(5, 5e13 / max(flops, 1.0))))
+
+    sel = gsr.select_config(M, N, K)
+    ref = gsr.gemm_scale_relu(a, b, alpha).clone()
+    torch.cuda.synchronize()
+    sel_us = time_calls(lambda: gsr.gemm_scale_relu(a, b, alpha, c=c, stream=stream), stream, steps)
+    log(f"[tune] {name} {M}x{N}x{K}: selector cfg {sel['id']} group {sel['group_m']} xcd {sel['xcd_remap']}"
+        f" {sel_us:.2f} us")
+
+    cands: List[dict] = []
+
+    def measure(cid: int, group_m: int, xcd: int) -> dict:
+        cfg = gsr.get_config(cid)
+        out = gsr.gemm_launch(a, b, alpha, cid, group_m, xcd, c=c, stream=stream)
+        torch.cuda.synchronize()
+        ok = close(out, ref)
+        us = time_calls(lambda: gsr.gemm_launch(a, b, alpha, cid, group_m, xcd, c=c, stream=stream),
+                        stream, steps)
+        rec = {"config_id": cid, "group_m": group_m, "xcd_remap": xcd, "us": round(us, 3),
+               "tflops": round(flops / (us * 1e-6) / 1e12, 2), "lds_bytes": cfg["lds_bytes"],
+               "tile": f"{cfg['block_m']}x{cfg['block_n']}x{cfg['block_k']}", "matches_selector_output": ok}
+        cands.append(rec)
+        return rec
+
+    # 1. every compiled configuration in its own launch order
+    for cid in range(gsr.num_configs()):
+        cfg = gsr.get_config(cid)
+        r = measure(cid, cfg["group_m"], cfg["xcd_remap"])
+        log(f"[tune]   cfg {cid:2d} {r['tile']:>11s} {r['us']:9.2f} us {r['tflops']:8.1f} TF/s"
+            f"{'' if r['matches_selector_output'] else '  OUTPUT MISMATCH'}")
+    # 2. launch order of the fastest few
+    best_ids = [r["config_id"] for r in sorted((r for r in cands if r["matches_selector_output"]),
+                                                 key=lambda r: r["us"])[:top]]
+    for cid in best_ids:
+        base = gsr.gemm_launch(a, b, alpha, cid, gsr.get_config(cid)["group_m"],
+                               gsr.get_config(cid)["xcd_remap"]).clone()
+        for gm in GROUPS:
+            for xcd in (0, 1):
+                cfg = gsr.get_config(cid)
+                if gm == cfg["group_m"] and xcd == cfg["xcd_remap"]:
+                    continue
+                r = measure(cid, gm, xcd)
+                same = torch.equal(c.view(torch.int16), base.view(torch.int16))
+                r["bitwise_equal_to_default_order"] = same
+                if not same:
+                    r["matches_selector_output"] = False
+                log(f"[tune]   cfg {cid:2d} group {gm:2d} xcd {xcd} {r['us']:9.2f} us"
+                    f"{'' if same else '  ORDER CHANGED THE RESULT'}")
+
+    valid = [r for r in cands if r["matches_selector_output"]]
+    best = min(valid, key=lambda r: r["us"])
+    kept = sel_us / best["us"] < 1.0 + min_gain
+    if kept:  # within timing noise of the selector: keep the selector's launch
+        best = {"config_id": sel["id"], "group_m": sel["group_m"], "xcd_remap": sel["xcd_remap"],
+                "us": round(sel_us, 3), "tflops": round(flops / (sel_us * 1e-6) / 1e12, 2),
+                "lds_bytes": gsr.get_config(sel["id"])["lds_bytes"], "selector_kept": True}
+    log(f"[tune] {name}: best cfg {best['config_id']} group {best['group_m']} xcd {best['xcd_remap']}"
+        f" {best['us']:.2f} us ({sel_us / best['us']:.3f}x the selector)"
+        f"{' -- selector kept (gain below the margin)' if kept else ''}")
+    return {"shape": name, "M": M, "N": N, "K": K, "alpha": alpha, "steps": steps,
+            "selector": {"config_id": sel["id"], "group_m": sel["group_m"], "xcd_remap": sel["xcd_remap"],
+                         "us": round(sel_us, 3)},
+            "best": best, "speedup_vs_selector": round(sel_us / best["us"], 4),
+            "pareto_time_vs_lds": pareto(valid), "candidates": cands}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--shapes", required=True, help="comma-separated MxNxK or workload names")
+    ap.add_argument("--out", required=True, help="tuning table to write (gsr_load_tuning format)")
+    ap.add_argument("--report", default=None, help="JSON report with every timing")
+    ap.add_argument("--top", type=int, default=3, help="configurations whose launch order is swept")
+    ap.add_argument("--min-gain", type=float, default=0.01,
+                    help="keep the selector's launch unless a candidate beats it by this fraction")
+    args = ap.parse_args(argv)
+
+    import tiled_dense_gemm_scale_amd as gsr
+
+    if not torch.cuda.is_available():
+        print("tune: no GPU visible", file=sys.stderr)
+        return 2
+    gsr.clear_tuning()  # the selector's own choice is the baseline
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    t0 = time.time()
+    results = [tune_shape(gsr, s.strip(), args.top, args.min_gain, log)
+               for s in args.shapes.split(",") if s.strip()]
+    props = torch.cuda.get_device_properties(0)
+    with open(args.out, "w") as f:
+        f.write(f"# gsr tuning table: {props.name} {getattr(props, 'gcnArchName', '')}, "
+                f"libgsr version {gsr.version()}\n")
+        f.write("# M N K config_id group_m xcd_remap    (us per call; speedup over the built-in selector)\n")
+        for r in results:
+            b = r["best"]
+            f.write(f"{r['M']} {r['N']} {r['K']} {b['config_id']} {b['group_m']} {b['xcd_remap']}"
+                    f"    # {r['shape']}: {b['us']} us, {r['speedup_vs_selector']}x\n")
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump({"device": props.name, "arch": getattr(props, "gcnArchName", ""),
+                       "library_version": gsr.version(), "seconds": round(time.time() - t0, 1),
+                       "shapes": results}, f, indent=1)
+    # the table must load back
+    gsr.load_tuning(args.out)
+    log(f"[tune] wrote {args.out} ({gsr.tuning_entries()} entries)")
+    gsr.clear_tuning()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
