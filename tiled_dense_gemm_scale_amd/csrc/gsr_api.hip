@@ -16,6 +16,7 @@
 #include "gsr_bt.hpp"
 #include "gsr_interleave.hpp"
 #include "gsr_ksplit.hpp"
+#include "gsr_dual.hpp"
 
 namespace {
 
@@ -50,6 +51,12 @@ hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
 hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dual(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_dual_kernel, dim3(grid), dim3(gsr::DualCfg::NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -124,6 +131,8 @@ const Entry kTable[] = {
     GSR_KSPLIT(17, 64, 32, 6, 4),
     GSR_KSPLIT(18, 32, 64, 6, 4),
     GSR_KSPLIT(19, 64, 64, 5, 4),            // one more stage in flight (160 KiB)
+    // explicit interleave, both operands copied to LDS, B by transpose reads
+    Entry{{20, 256, 256, 64, 2, 2, 2, 4, 1, gsr::DualCfg::LDS_BYTES}, launch_dual, launch_staged<256, 256, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 

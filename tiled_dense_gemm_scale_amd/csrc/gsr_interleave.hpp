@@ -74,6 +74,97 @@ __device__ __forceinline__ void wait_vmcnt_b(u32x4 (&r)[8])
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// The epilogue of the 256x256 kernels: scale, ReLU (or the variant: scale,
+// bias, activation) and round in registers, then pass each wave's 128x128
+// fp16 sub-tile through its own 32 KB of LDS so that the global stores write
+// whole 256-byte row segments (16 lanes per row) instead of 16 bytes in each
+// of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at physical
+// chunk c ^ (r % 16).  Called once every wave's copies have been drained.
+__device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&acc)[IlvCfg::TN][IlvCfg::TM],
+                                             uint8_t* smem, int m0, int n0, int wm, int wn, int wave,
+                                             uint32_t frow, uint32_t fhi)
+{
+    using T = IlvCfg;
+    constexpr int TM = T::TM, TN = T::TN;
+    const uint32_t lane = (uint32_t)(threadIdx.x & 63);
+    const uint32_t N = (uint32_t)p.N;
+    static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
+    // The variant's bias values for the lane's 16 column groups are requested
+    // before the barrier, so their latency overlaps it.
+    const bool plain = plain_epilogue(p);
+    f32x4 bvs[TN][4];
+    {
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const bool load = !plain && p.bias != nullptr;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bvs[a][g] = load ? bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi)
+                                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    lds_barrier();  // every wave is past its last operand read
+    const float alpha = p.alpha;
+    uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
+    auto stage4 = [&](int a, int b, int g, half4 h) {
+        const uint32_t r = (uint32_t)b * 32u + frow;
+        const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
+        *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
+    };
+    if (plain) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
+#pragma unroll
+            for (int b = 0; b < TM; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    half4 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = acc[a][b][4 * g + i] * alpha;
+                        h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                    }
+                    stage4(a, b, g, h);
+                }
+            }
+        }
+    } else {
+        // act(alpha * acc + bias)
+        with_activation(p.act, [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 bv = bvs[a][g];
+#pragma unroll
+                    for (int b = 0; b < TM; ++b) {
+                        const f32x16 av = acc[a][b];
+                        f32x4 sv;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
+                        stage4(a, b, g, epilogue4<ACT>(sv, alpha, bv));
+                    }
+                }
+            }
+        });
+    }
+    // The reads below take what other lanes of this wave wrote: LDS keeps a
+    // wave's accesses in order, so only the compiler must not move them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
+    const uint32_t sc = (uint32_t)lane & 15u;
+    const int n = n0 + wn * T::WTN + 8 * (int)sc;
+#pragma unroll
+    for (int j = 0; j < T::WTM / 4; ++j) {
+        const uint32_t r = 4u * (uint32_t)j + ((uint32_t)lane >> 4);
+        const u32x4 v = *(const u32x4*)(ep + r * 256u + ((sc ^ (r & 15u)) << 4));
+        const int m = m0 + wm * T::WTM + (int)r;
+        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+    }
+}
+
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_scale_relu_ilv_kernel(Problem p)
 {
@@ -304,86 +395,7 @@ gemm_scale_relu_ilv_kernel(Problem p)
     wait_vmcnt_b<0>(breg);
 
     // ---- epilogue ------------------------------------------------------------
-    // Scale, ReLU (or the variant: scale, bias, activation) and round in
-    // registers, then pass the wave's 128x128 fp16 sub-tile through its own
-    // 32 KB of LDS so that the global stores write whole 256-byte row
-    // segments (16 lanes per row) instead of 16 bytes in each of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at
-    // physical chunk c ^ (r % 16).
-    static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
-    // The variant's bias values for the lane's 16 column groups are requested
-    // before the barrier, so their latency overlaps it.
-    const bool plain = plain_epilogue(p);
-    f32x4 bvs[TN][4];
-    {
-        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const bool load = !plain && p.bias != nullptr;
-#pragma unroll
-        for (int a = 0; a < TN; ++a)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                bvs[a][g] = load ? bias4(rbias, n0 + wn * T::WTN + a * 32 + 8 * g + 4 * (int)fhi)
-                                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    lds_barrier();  // every wave is past its last operand read
-    const float alpha = p.alpha;
-    uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
-    auto stage4 = [&](int a, int b, int g, half4 h) {
-        const uint32_t r = (uint32_t)b * 32u + frow;
-        const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
-        *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
-    };
-    if (plain) {
-#pragma unroll
-        for (int a = 0; a < TN; ++a) {
-#pragma unroll
-            for (int b = 0; b < TM; ++b) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    half4 h;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = acc[a][b][4 * g + i] * alpha;
-                        h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
-                    }
-                    stage4(a, b, g, h);
-                }
-            }
-        }
-    } else {
-        // act(alpha * acc + bias)
-        with_activation(p.act, [&](auto act_tag) {
-            constexpr int ACT = decltype(act_tag)::value;
-#pragma unroll
-            for (int a = 0; a < TN; ++a) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 bv = bvs[a][g];
-#pragma unroll
-                    for (int b = 0; b < TM; ++b) {
-                        const f32x16 av = acc[a][b];
-                        f32x4 sv;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sv[i] = av[4 * g + i];
-                        stage4(a, b, g, epilogue4<ACT>(sv, alpha, bv));
-                    }
-                }
-            }
-        });
-    }
-    // The reads below take what other lanes of this wave wrote: LDS keeps a
-    // wave's accesses in order, so only the compiler must not move them.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
-    const uint32_t sc = (uint32_t)lane & 15u;
-    const int n = n0 + wn * T::WTN + 8 * (int)sc;
-#pragma unroll
-    for (int j = 0; j < T::WTM / 4; ++j) {
-        const uint32_t r = 4u * (uint32_t)j + ((uint32_t)lane >> 4);
-        const u32x4 v = *(const u32x4*)(ep + r * 256u + ((sc ^ (r & 15u)) << 4));
-        const int m = m0 + wm * T::WTM + (int)r;
-        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
-    }
+    ilv_epilogue(p, acc, smem, m0, n0, wm, wn, wave, frow, fhi);
 }
 
 }  // namespace gsr
