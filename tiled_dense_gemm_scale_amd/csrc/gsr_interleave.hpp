@@ -275,10 +275,12 @@ gemm_scale_relu_ilv_kernel(Problem p)
     auto read_y = [&](int S, int ks, int b, half8& dst) {
         dst = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::A_BYTES + y_addr[ks][b]));
     };
-    // unit i of a substep reads operand i of the next one (4 x's then 4 y's)
+    // read i (0..7) of the next substep's operands, in the order its MFMAs
+    // need them: x0, y0..y3 (units 0-3 use x0 with every y), then x1..x3
     auto read_next = [&](int S, int ks, int i, half8 (&xs)[TN], half8 (&ys)[TM]) {
-        if (i < TN) read_x(S, ks, i, xs[i]);
-        else read_y(S, ks, i - TN, ys[i - TN]);
+        if (i == 0) read_x(S, ks, 0, xs[0]);
+        else if (i <= TM) read_y(S, ks, i - 1, ys[i - 1]);
+        else read_x(S, ks, i - TM, xs[i - TM]);
     };
     auto mma = [&](int i, const half8 (&xs)[TN], const half8 (&ys)[TM]) {
         const int a = i / TM, b = i % TM;

@@ -252,7 +252,16 @@ gemm_scale_relu_ksplit_kernel(Problem p)
 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
     const float alpha = p.alpha;
-    // unit u = blk*4 + g goes to wave u % 4
+    // unit u = blk*4 + g goes to wave u % 4.  All of this wave's partial
+    // reads are issued before any sum, so their latencies overlap.
+    f32x4 part[NB][NW];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int u = j * NW + wave;
+        const int blk = u >> 2, g = u & 3;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) part[j][w] = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
+    }
     with_activation(p.act, [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -263,9 +272,8 @@ gemm_scale_relu_ksplit_kernel(Problem p)
             float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const f32x4 v = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] += v[i];
+                for (int i = 0; i < 4; ++i) s[i] += part[j][w][i];
             }
             const int m = m0 + b * 32 + (int)frow;
             const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
