@@ -106,6 +106,19 @@ def bias_input(N: int, seed: int = 0, std: float = 1.0, integer: bool = False) -
     return (torch.randn(N, generator=g, dtype=torch.float32) * std).half()
 
 
+def pattern_inputs(M: int, N: int, K: int, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Integer-valued fp16 inputs with no random draw, built where they are
+    used (so multi-GiB operands need no host copy to create):
+    A[m,k] = ((7m + 13k) mod 9) - 4 and B[k,n] = ((5k + 11n) mod 7) - 3.
+    Every fp32 partial sum stays an exact integer while |sums| < 2^24."""
+    m = torch.arange(M, device=device, dtype=torch.int64)[:, None]
+    k = torch.arange(K, device=device, dtype=torch.int64)
+    a = ((7 * m + 13 * k[None, :]) % 9 - 4).to(torch.float16)
+    n = torch.arange(N, device=device, dtype=torch.int64)[None, :]
+    b = ((5 * k[:, None] + 11 * n) % 7 - 3).to(torch.float16)
+    return a, b
+
+
 def sample_points(M: int, N: int, count: int = 4096, seed: int = 1,
                   extra_rows: Optional[list] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Output coordinates to check on the largest shapes: the four corners,
