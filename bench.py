@@ -366,7 +366,13 @@ def main(argv=None) -> int:
             "tuning": os.path.relpath(args.tuning, ROOT) if args.tuning else None,
             "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
-            "device": {"cus": dinfo.get("cus"), "max_clock_mhz": (dinfo["clock_khz"] / 1000.0) if "clock_khz" in dinfo else None},
+            "device": {"cus": dinfo.get("cus"), "max_clock_mhz": (dinfo["clock_khz"] / 1000.0) if "clock_khz" in dinfo else None,
+                       # dense fp16: 4096 FLOP per clock per CU (256 per SIMD lane-op x 16) at the reported clock
+                       "peak_tflops_from_device": (round(dinfo["cus"] * 4096 * dinfo["clock_khz"] * 1e3 / 1e12, 1)
+                                                   if "cus" in dinfo and "clock_khz" in dinfo else None)},
+            "caches": "warm: the timed calls reuse the same A and B, which stay in the 256 MB last-level cache "
+                      "when they fit (all workloads but 16384^3)",
+            "gpu_over_oracle": (round(tflops / cpu["value"], 1) if cpu else None),
             **context,
         },
         "roofline": roofline,
