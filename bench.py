@@ -134,24 +134,42 @@ def cpu_baseline(w, a, b, target_s: float, epilogue: str = "relu", bias=None):
         else:
             orc.gemm_bias_act(a_bits[:rows], b_bits, bias_bits, w.alpha, act, nthreads=threads)
 
-    # calibrate on a few rows, then size the sample
-    rows = min(w.M, max(threads, 8))
+    # size the sample from two timed runs (each run also decodes all of B: a
+    # fixed cost beside the per-row cost); a workload the oracle finishes
+    # whole in well under the target is repeated instead
+    def timed(rows):
+        t0 = time.perf_counter()
+        run(rows)
+        return time.perf_counter() - t0
+
+    R1 = min(w.M, max(threads, 8))
+    t1 = timed(R1)
+    if R1 >= w.M:
+        per_row, fixed = t1 / R1, 0.0
+    else:
+        R2 = min(w.M, R1 * 4)
+        t2 = timed(R2)
+        per_row = max((t2 - t1) / (R2 - R1), 1e-9)
+        fixed = max(t1 - per_row * R1, 0.0)
+    R = int(min(w.M, max(R1, (target_s - fixed) / per_row)))
+    if R < w.M:
+        R = max(threads, (R // threads) * threads)
+        reps = 1
+    else:
+        R = w.M
+        reps = int(max(1, min(1000, round(target_s / (fixed + per_row * w.M)))))
     t0 = time.perf_counter()
-    run(rows)
-    t_cal = time.perf_counter() - t0
-    per_row = t_cal / rows
-    R = int(min(w.M, max(rows, target_s / max(per_row, 1e-9))))
-    R = max(threads, (R // threads) * threads) if R < w.M else w.M
-    t0 = time.perf_counter()
-    run(R)
+    for _ in range(reps):
+        run(R)
     t = time.perf_counter() - t0
-    flops = 2.0 * R * w.N * w.K
+    flops = 2.0 * R * w.N * w.K * reps
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"rows 0..{R - 1} of C ({R}x{w.N} outputs, K={w.K}), full fp64 oracle, {t:.2f} s",
+        "sample": (f"rows 0..{R - 1} of C ({R}x{w.N} outputs, K={w.K})" + (f", {reps} times" if reps > 1 else "")
+                   + f", full fp64 oracle, {t:.2f} s"),
     }
 
 
