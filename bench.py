@@ -194,6 +194,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-context", action="store_true", help="skip the dispatch-floor measurement")
     ap.add_argument("--no-torch-context", action="store_true",
                     help="skip timing torch's unfused matmul -> mul -> relu and its plain fp16 matmul")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single calls with L2 and the last-level cache flushed before each "
+                         "(context only; eager launches, so each time holds one dispatch)")
     ap.add_argument("--zero-input", action="store_true",
                     help="also time the same kernel on all-zero inputs (runs the timed kernel again, "
                          "so leave it off when profiling per-kernel averages)")
@@ -317,6 +320,34 @@ def main(argv=None) -> int:
         context["speedup_vs_torch_unfused"] = round(tu / ms, 3)
         log(f"[bench] torch unfused {tu * 1e3:.2f} us ({context['torch_unfused_tflops']} TFLOP/s), "
             f"torch matmul only {tm * 1e3:.2f} us ({context['torch_matmul_only_tflops']} TFLOP/s)")
+    if args.cold:
+        # Before every call: write 512 MiB (evicts A, B and C from L2, 4 MB
+        # per XCD, and from the 256 MB last-level cache), then read another
+        # 512 MiB one element per 64 bytes (every line is fetched, so the
+        # dirty lines of the write are written back now, not during the
+        # call).  The call alone is timed with events on the launch stream.
+        flush = torch.empty(256 * 1024 * 1024, dtype=torch.float16, device=dev)
+        clean = torch.ones(256 * 1024 * 1024, dtype=torch.float16, device=dev)
+        sink = torch.empty(clean.numel() // 32, dtype=torch.float16, device=dev)
+        cold = []
+        with torch.cuda.stream(stream):
+            for i in range(max(5, min(args.steps, 30))):
+                flush.fill_(float(i))
+                sink.copy_(clean.view(-1, 32)[:, 0])
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+                cold.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in cold)[len(cold) // 2]
+        del flush, clean, sink
+        torch.cuda.empty_cache()
+        context["cold_us_per_call"] = round(cold_ms * 1e3, 3)
+        context["cold_tflops"] = round(w.flops / (cold_ms * 1e-3) / 1e12, 3)
+        log(f"[bench] cold caches (median of {len(cold)}): {cold_ms * 1e3:.2f} us/call "
+            f"({context['cold_tflops']} TFLOP/s)")
     if graph is not None and args.zero_input:
         za = torch.zeros_like(a)
         zb = torch.zeros_like(b)
