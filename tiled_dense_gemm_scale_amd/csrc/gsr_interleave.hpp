@@ -11,9 +11,10 @@
 // Per K-step t (BK = 64, four 16-k substeps of 16 MFMAs each), units carry:
 //   substep 0: the next substep's operand reads, then the byte-permute
 //              transpose of the B block of step t+1;
-//   substep 1: the next substep's operand reads alternating with the
-//              transposed B writes of step t+1 and the B loads of step t+2;
-//   substep 2: the next substep's operand reads;
+//   substep 1: the next substep's operand reads alternating with the B loads
+//              of step t+2;
+//   substep 2: the next substep's operand reads alternating with the
+//              transposed B writes of step t+1;
 //   substep 3: four MFMAs, the wait + barrier that publishes step t+1's
 //              buffers, then the first operand reads of step t+1 and the A
 //              copies of step t+2 (buffer_load ... lds) into the stage that
@@ -317,26 +318,26 @@ gemm_scale_relu_ilv_kernel(Problem p)
             }
             sched_fence();
         }
-        // substep 1: reads for substep 2 on even units; transposed B(t+1)
-        // stores into stage SN and the loads of B(t+2) on odd units
+        // substep 1: reads for substep 2 on even units, the loads of B(t+2)
+        // on odd units
         {
             const i32x4 rb = b_rsrc(k2);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 mma(i, xf[1], yf[1]);
                 if ((i & 1) == 0) read_next(S, 2, i >> 1, xf[0], yf[0]);
-                else {
-                    *(u32x4*)(smem + SN * T::B_BYTES + bw_addr[i >> 1]) = bcol[i >> 1];
-                    breg[i >> 1] = load16(rb, b_voff[i >> 1]);
-                }
+                else breg[i >> 1] = load16(rb, b_voff[i >> 1]);
                 sched_fence();
             }
         }
-        // substep 2: reads for substep 3
+        // substep 2: reads for substep 3 on even units, the transposed B(t+1)
+        // stores into stage SN on odd units (the LDS work of a step then
+        // spreads as 8 / 8 / 16 / 16 operations over its four substeps)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mma(i, xf[0], yf[0]);
             if ((i & 1) == 0) read_next(S, 3, i >> 1, xf[1], yf[1]);
+            else *(u32x4*)(smem + SN * T::B_BYTES + bw_addr[i >> 1]) = bcol[i >> 1];
             sched_fence();
         }
         // substep 3: publish step t+1 (the copies of A(t+1) landed: only the 8
