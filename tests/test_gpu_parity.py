@@ -48,6 +48,17 @@ def test_workload_full(gsr, orc, name):
     PT.assert_parity(name, got, ref)
 
 
+def test_skinny_full(gsr, orc):
+    """The HBM-bound skinny class (16 x 11008 x 4096, B ~ N(0, 1/K)), every
+    output, in the selector's launch."""
+    w = W.SKINNY
+    a, b = W.workload_inputs(w)
+    say(f"[gpu] {w.name} {w.M}x{w.N}x{w.K} alpha={w.alpha} selector")
+    got = PT.run_gpu(a, b, w.alpha)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), w.alpha)
+    PT.assert_parity(w.name, got, ref)
+
+
 @pytest.mark.parametrize("name", ["square_4096", "llm_mlp_4097x11008x4096", "square_16384"])
 def test_workload_sampled(gsr, orc, name):
     w = W.WORKLOADS[name]
@@ -96,6 +107,29 @@ def test_ragged_every_config(gsr, orc, shape):
         say(f"[gpu] ragged {shape} config {cid}")
         got = PT.run_gpu(a, b, 0.5, config_id=cid)
         PT.assert_parity(f"{shape} cfg{cid}", got, ref)
+
+
+# K-split tiles with separate copy waves against the four-wave K-split kernel
+# of the same tile: same K split, same summation order, so the same bits.
+# K covers 1, 2, 3, 4 and 9 steps of 128; M and N ragged against the tile.
+COPY_WAVE_TWINS = [(21, 16), (22, 18)]
+
+
+@pytest.mark.parametrize("shape", [(64, 64, 8), (100, 72, 136), (1024, 1024, 264), (33, 200, 392),
+                                   (520, 1000, 1032), (16, 11008, 4096)], ids=lambda s: "x".join(map(str, s)))
+def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
+    M, N, K = shape
+    a, b = W.normal_inputs(M, N, K, seed=M + 3 * N + 5 * K)
+    ad, bd = a.to(DEV), b.to(DEV)
+    for new, old in COPY_WAVE_TWINS:
+        say(f"[gpu] copy-wave K split {shape}: config {new} vs {old}")
+        c_new = gsr.gemm_scale_relu_ex(ad, bd, 0.5, new).clone()
+        c_old = gsr.gemm_scale_relu_ex(ad, bd, 0.5, old).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(c_new.view(torch.int16), c_old.view(torch.int16)), (shape, new, old)
+    if M * N * K <= 2e8:  # and the 64x64 copy-wave tile against the oracle
+        ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
+        PT.assert_parity(f"{shape} cfg21", PT.run_gpu(a, b, 0.5, config_id=21), ref)
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 200), (257, 263, 129), (1024, 1024, 512),

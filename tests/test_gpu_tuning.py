@@ -24,7 +24,7 @@ def gsr(native):
     g.clear_tuning()
 
 
-@pytest.mark.parametrize("cid", [15, 16, 7, 9, 18])
+@pytest.mark.parametrize("cid", [15, 16, 7, 9, 18, 21, 22])
 def test_launch_order_does_not_change_results(gsr, orc, cid):
     M, N, K = 700, 1100, 264
     a, b = W.normal_inputs(M, N, K, seed=cid)
