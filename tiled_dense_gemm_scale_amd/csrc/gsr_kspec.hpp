@@ -15,10 +15,16 @@
 //               the copies of step t + DEPTH into the buffer step t - 1 used.
 //   MFMA wave:  barrier t (after its reads of step t - 1 have returned); read
 //               step t; MFMAs of step t - 1.
-// Tile, LDS layouts, the K split among the MFMA waves (wave w takes 16-k
-// substeps w and w + 4 of each 128-deep step) and the reduction of the four
-// partial tiles through LDS are those of the four-wave K-split kernel, so the
-// two kernels produce the same bits.
+// Tile, LDS operand layouts and the K split among the MFMA waves (wave w
+// takes 16-k substeps w and w + 4 of each 128-deep step) are those of the
+// four-wave K-split kernel, and the four partial tiles are summed in the same
+// order, so the two kernels produce the same bits.  The sum runs on all eight
+// waves: the MFMA waves write their partial tiles to LDS as row-major fp32
+// rows (16-byte chunks XOR-swizzled by row, so neither the writes from the
+// MFMA lane layout nor the row reads conflict), then each thread sums one
+// row's eight consecutive outputs and stores them with one 16-byte store;
+// eight lanes cover a 128-byte row of a 64-wide tile, so the stores write
+// whole lines instead of 16-byte pieces of 32 rows.
 #pragma once
 
 #include "gsr_ksplit.hpp"
@@ -30,7 +36,7 @@ __global__ void __launch_bounds__(512)
 gemm_scale_relu_kspec_kernel(Problem p)
 {
     using T = KsCfg<BM, BN, STAGES>;
-    constexpr int BK = T::BK, NW = T::NW, CHA = T::CHA, CHN = T::CHN, TM = T::TM, TN = T::TN, NB = T::NB;
+    constexpr int BK = T::BK, NW = T::NW, CHA = T::CHA, CHN = T::CHN, TM = T::TM, TN = T::TN;
     static_assert(DEPTH >= 1 && DEPTH <= STAGES - 1, "steps in flight");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
@@ -45,6 +51,10 @@ gemm_scale_relu_kspec_kernel(Problem p)
     tile_of(blockIdx.x, gridDim.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int ksteps = (p.K + BK - 1) / BK;
+
+    using Sum = KsSum<BM, BN, NW, 512>;  // the cross-wave sum runs on all eight waves
+    static_assert(Sum::BYTES <= T::LDS_BYTES, "partial tiles fit in LDS");
+    f32x4 bvs[Sum::NU][2];
 
     if (copier) {
         // ---- copy waves ----------------------------------------------------------
@@ -103,168 +113,103 @@ gemm_scale_relu_kspec_kernel(Problem p)
             lds_barrier();
             if (t + DEPTH < ksteps) issue((t + DEPTH) % STAGES, (t + DEPTH) * BK);
         }
+        Sum::load_bias(p, tid, n0, bvs);
+        wait_vmcnt<0>();
         lds_barrier();  // the MFMA waves' partial tiles may now overwrite the buffers
-        lds_barrier();  // partial tiles written
-        return;
-    }
-
-    // ---- MFMA waves ---------------------------------------------------------------
-    const uint32_t frow = lane & 31, fhi = lane >> 5;
-    uint32_t y_off[2][TM];  // A rows
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int b = 0; b < TM; ++b) {
-            const uint32_t r = b * 32 + frow;
-            const uint32_t c = 2u * (uint32_t)(wave + 4 * h) + fhi;
-            y_off[h][b] = r * (BK * 2) + ((c ^ swz_a16(r)) << 4);
-        }
-    // transpose reads of B: 16-lane group G, i = l%16, e = i/4, q = i%4
-    const uint32_t G = lane >> 4, li = lane & 15, e4 = li >> 2, q4 = li & 3;
-    uint32_t x_off[2][2][TN];  // [substep half][read 0/1][n block]
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-            for (int a = 0; a < TN; ++a) {
-                const uint32_t k = 16u * (uint32_t)(wave + 4 * h) + 8u * (G >> 1) + 4u * rd + e4;
-                const uint32_t chunk = (uint32_t)(a * 32 + 16 * (G & 1)) / 8 + (q4 >> 1);
-                x_off[h][rd][a] = (uint32_t)T::A_BYTES + k * (BN * 2) + ((chunk ^ swz_b<CHN>(k)) << 4) + (q4 & 1) * 8;
-            }
-
-    f32x16 acc[TN][TM];
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    half8 xs0[2][TN], ys0[2][TM], xs1[2][TN], ys1[2][TM];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int a = 0; a < TN; ++a) xs0[h][a] = xs1[h][a] = (half8)(_Float16)0.0f;
-#pragma unroll
-        for (int b = 0; b < TM; ++b) ys0[h][b] = ys1[h][b] = (half8)(_Float16)0.0f;
-    }
-    auto read_step = [&](int stage, half8 (&xs)[2][TN], half8 (&ys)[2][TM]) {
-        const uint8_t* base = smem + stage * T::STAGE_BYTES;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int b = 0; b < TM; ++b) ys[h][b] = __builtin_bit_cast(half8, *(const u32x4*)(base + y_off[h][b]));
-#pragma unroll
-            for (int a = 0; a < TN; ++a) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][0][a]));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][1][a]));
-                xs[h][a] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-        }
-    };
-    auto mma_step = [&](const half8 (&xs)[2][TN], const half8 (&ys)[2][TM]) {
+    } else {
+        // ---- MFMA waves ---------------------------------------------------------------
+        const uint32_t frow = lane & 31, fhi = lane >> 5;
+        uint32_t y_off[2][TM];  // A rows
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int a = 0; a < TN; ++a)
-#pragma unroll
-                for (int b = 0; b < TM; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xs[h][a], ys[h][b], acc[a][b], 0, 0, 0);
-    };
-
-    // step t is read into set t & 1 and multiplied one iteration later
-    int t = 0;
-    for (; t + 1 < ksteps; t += 2) {
-        lds_barrier();
-        read_step(t % STAGES, xs0, ys0);
-        if (t > 0) mma_step(xs1, ys1);
-        lds_barrier();
-        read_step((t + 1) % STAGES, xs1, ys1);
-        mma_step(xs0, ys0);
-    }
-    if (t < ksteps) {  // odd step count: one more even step
-        lds_barrier();
-        read_step(t % STAGES, xs0, ys0);
-        if (t > 0) mma_step(xs1, ys1);
-        mma_step(xs0, ys0);
-    } else if (ksteps > 0) {
-        mma_step(xs1, ys1);
-    }
-
-    // ---- sum the four partial tiles through LDS ---------------------------------
-    const bool plain = plain_epilogue(p);
-    f32x4 bvs[NB];
-    {
-        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const bool load = !plain && p.bias != nullptr;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int u = j * NW + wave;
-            const int blk = u >> 2, g = u & 3;
-            const int n = n0 + (blk / TM) * 32 + 8 * g + 4 * (int)fhi;
-            bvs[j] = load ? bias4(rbias, n) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    }
-    wait_vmcnt<0>();
-    lds_barrier();  // every wave is done with the operand buffers
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int slot = (wave * NB + a * TM + b) * 4 + g;
-                const f32x16 av = acc[a][b];
-                f32x4 v;
-                if (g == 0) v = __builtin_shufflevector(av, av, 0, 1, 2, 3);
-                else if (g == 1) v = __builtin_shufflevector(av, av, 4, 5, 6, 7);
-                else if (g == 2) v = __builtin_shufflevector(av, av, 8, 9, 10, 11);
-                else v = __builtin_shufflevector(av, av, 12, 13, 14, 15);
-                *(f32x4*)(smem + slot * 1024 + lane * 16) = v;
+            for (int b = 0; b < TM; ++b) {
+                const uint32_t r = b * 32 + frow;
+                const uint32_t c = 2u * (uint32_t)(wave + 4 * h) + fhi;
+                y_off[h][b] = r * (BK * 2) + ((c ^ swz_a16(r)) << 4);
             }
-    lds_barrier();
-
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
-    const float alpha = p.alpha;
-    f32x4 part[NB][NW];
+        // transpose reads of B: 16-lane group G, i = l%16, e = i/4, q = i%4
+        const uint32_t G = lane >> 4, li = lane & 15, e4 = li >> 2, q4 = li & 3;
+        uint32_t x_off[2][2][TN];  // [substep half][read 0/1][n block]
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int u = j * NW + wave;
-        const int blk = u >> 2, g = u & 3;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int w = 0; w < NW; ++w) part[j][w] = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
-    }
-    with_activation(p.act, [&](auto act_tag) {
-        constexpr int ACT = decltype(act_tag)::value;
+            for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int u = j * NW + wave;
-            const int blk = u >> 2, g = u & 3;
-            const int a = blk / TM, b = blk % TM;
-            float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] += part[j][w][i];
-            }
-            const int m = m0 + b * 32 + (int)frow;
-            const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
-            half4 hv;
-            if (plain) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = s[i] * alpha;
-                    hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
+                for (int a = 0; a < TN; ++a) {
+                    const uint32_t k = 16u * (uint32_t)(wave + 4 * h) + 8u * (G >> 1) + 4u * rd + e4;
+                    const uint32_t chunk = (uint32_t)(a * 32 + 16 * (G & 1)) / 8 + (q4 >> 1);
+                    x_off[h][rd][a] = (uint32_t)T::A_BYTES + k * (BN * 2) + ((chunk ^ swz_b<CHN>(k)) << 4) + (q4 & 1) * 8;
                 }
-            } else {
-                const f32x4 sv = {s[0], s[1], s[2], s[3]};
-                hv = epilogue4<ACT>(sv, alpha, bvs[j]);
-            }
-            const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);
+
+        f32x16 acc[TN][TM];
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int b = 0; b < TM; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+        half8 xs0[2][TN], ys0[2][TM], xs1[2][TN], ys1[2][TM];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int a = 0; a < TN; ++a) xs0[h][a] = xs1[h][a] = (half8)(_Float16)0.0f;
+#pragma unroll
+            for (int b = 0; b < TM; ++b) ys0[h][b] = ys1[h][b] = (half8)(_Float16)0.0f;
         }
-    });
+        auto read_step = [&](int stage, half8 (&xs)[2][TN], half8 (&ys)[2][TM]) {
+            const uint8_t* base = smem + stage * T::STAGE_BYTES;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int b = 0; b < TM; ++b) ys[h][b] = __builtin_bit_cast(half8, *(const u32x4*)(base + y_off[h][b]));
+#pragma unroll
+                for (int a = 0; a < TN; ++a) {
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][0][a]));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + x_off[h][1][a]));
+                    xs[h][a] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            }
+        };
+        auto mma_step = [&](const half8 (&xs)[2][TN], const half8 (&ys)[2][TM]) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int a = 0; a < TN; ++a)
+#pragma unroll
+                    for (int b = 0; b < TM; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xs[h][a], ys[h][b], acc[a][b], 0, 0, 0);
+        };
+
+        // step t is read into set t & 1 and multiplied one iteration later
+        int t = 0;
+        for (; t + 1 < ksteps; t += 2) {
+            lds_barrier();
+            read_step(t % STAGES, xs0, ys0);
+            if (t > 0) mma_step(xs1, ys1);
+            lds_barrier();
+            read_step((t + 1) % STAGES, xs1, ys1);
+            mma_step(xs0, ys0);
+        }
+        if (t < ksteps) {  // odd step count: one more even step
+            lds_barrier();
+            read_step(t % STAGES, xs0, ys0);
+            if (t > 0) mma_step(xs1, ys1);
+            mma_step(xs0, ys0);
+        } else if (ksteps > 0) {
+            mma_step(xs1, ys1);
+        }
+
+        Sum::load_bias(p, tid, n0, bvs);
+        wait_vmcnt<0>();
+        lds_barrier();  // every wave is done with the operand buffers
+        Sum::write(smem, acc, wave, lane);
+    }  // MFMA waves
+    lds_barrier();  // partial tiles written
+
+    // ---- every wave: sum, epilogue, one 16-byte store per unit --------------------
+    Sum::sum_store(p, smem, tid, m0, n0, bvs);
 }
 
 }  // namespace gsr

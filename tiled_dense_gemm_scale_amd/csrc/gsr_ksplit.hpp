@@ -17,10 +17,10 @@
 //    column.
 //  * The operand reads of step t are issued right after the barrier that
 //    publishes step t, and the MFMAs of step t-1 run behind them.
-//  * At the end the four partial tiles are summed through LDS in the MFMA
-//    lane layout (each 1 KiB write and read is contiguous), and each wave
-//    stores a quarter of the tile: scale, clamp at zero, round to fp16 (or
-//    the epilogue variant: scale, bias, activation).
+//  * At the end the four partial tiles are summed through LDS (KsSum below):
+//    each thread sums one row's eight consecutive outputs over the waves,
+//    applies the epilogue (scale, clamp at zero, round to fp16; or scale,
+//    bias, activation) and writes them with one 16-byte store.
 #pragma once
 
 #include "gsr_pipeline.hpp"
@@ -43,7 +43,6 @@ struct KsCfg {
     static constexpr int LOADS = A_PER + B_PER;
     static_assert(BM % 32 == 0 && BN % 32 == 0 && CHN >= 4, "tile");
     static_assert((A_BYTES / 1024) % NW == 0 && (B_BYTES / 1024) % NW == 0, "copies split over waves");
-    static_assert((NB * 4) % NW == 0, "reduction units split over waves");
     static_assert(STAGES >= 2 && LDS_BYTES <= 163840, "LDS");
 };
 
@@ -51,12 +50,126 @@ struct KsCfg {
 // consecutive rows read at one logical chunk hit 16 distinct positions.
 __device__ __forceinline__ uint32_t swz_a16(uint32_t r) { return (r ^ (r >> 4)) & 15u; }
 
+// ---- the cross-wave sum of the K-split partial tiles ------------------------
+// Each of the NW waves writes its BM x BN fp32 partial tile to LDS as
+// row-major rows of BN*4 bytes whose 16-byte chunks are XOR-swizzled by row
+// (chunk c of row m sits at c ^ (m mod chunks-per-row)): the writes from the
+// MFMA lane layout (16 lanes = 16 rows at distinct chunks) and the row reads
+// (8 lanes = 8 consecutive chunks of one row; the next 8 lanes read the next
+// row, whose swizzle lands on the other half of the banks) do not conflict.
+// A sum unit is one row's eight consecutive outputs: its chunks are summed
+// over the waves in wave order (the same order for every element), then the
+// epilogue runs and one 16-byte store writes the unit.  Consecutive threads
+// take consecutive units, so the stores of a wave cover whole rows.
+template <int BM, int BN, int NW, int NT>
+struct KsSum {
+    static constexpr int QN = BN / 8;               // units per tile row
+    static constexpr int UNITS = BM * QN;
+    static constexpr int NU = (UNITS + NT - 1) / NT;  // units per thread
+    static constexpr int CPR = BN / 4;              // 16-byte chunks per partial row
+    static constexpr int PART_BYTES = BM * BN * 4;
+    static constexpr int BYTES = NW * PART_BYTES;
+    static_assert(BN % 32 == 0 && BM % 32 == 0, "tile");
+
+    __device__ static uint32_t addr(int w, int m, int chunk)
+    {
+        return (uint32_t)(w * PART_BYTES + m * (BN * 4)) + ((uint32_t)(chunk ^ (m & (CPR - 1))) << 4);
+    }
+
+    // bias values of this thread's units (zeros where the epilogue has none)
+    __device__ static void load_bias(const Problem& p, int tid, int n0, f32x4 (&bvs)[NU][2])
+    {
+        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
+        const bool load = !plain_epilogue(p) && p.bias != nullptr;
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int u = tid + NT * j;
+            const int n = n0 + 8 * (u % QN);
+            const bool ok = load && u < UNITS;
+            bvs[j][0] = ok ? bias4(rbias, n) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            bvs[j][1] = ok ? bias4(rbias, n + 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+
+    // wave w's partial tile: MFMA block (a, b), registers 4g..4g+3 of lane l
+    // hold row b*32 + l%32, columns a*32 + 8g + 4*(l/32) .. +3, i.e. fp32
+    // chunk 8a + 2g + l/32 of that row
+    template <int TN, int TM>
+    __device__ static void write(uint8_t* smem, const f32x16 (&acc)[TN][TM], int w, int lane)
+    {
+        const int frow = lane & 31, fhi = lane >> 5;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int b = 0; b < TM; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 av = acc[a][b];
+                    f32x4 v;
+                    if (g == 0) v = __builtin_shufflevector(av, av, 0, 1, 2, 3);
+                    else if (g == 1) v = __builtin_shufflevector(av, av, 4, 5, 6, 7);
+                    else if (g == 2) v = __builtin_shufflevector(av, av, 8, 9, 10, 11);
+                    else v = __builtin_shufflevector(av, av, 12, 13, 14, 15);
+                    *(f32x4*)(smem + addr(w, b * 32 + frow, 8 * a + 2 * g + fhi)) = v;
+                }
+    }
+
+    __device__ static void sum_store(const Problem& p, const uint8_t* smem, int tid, int m0, int n0,
+                                     const f32x4 (&bvs)[NU][2])
+    {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
+        const float alpha = p.alpha;
+        const bool plain = plain_epilogue(p);
+        with_activation(p.act, [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+            for (int j = 0; j < NU; ++j) {
+                const int u = tid + NT * j;
+                if (UNITS % NT != 0 && u >= UNITS) break;
+                const int mr = u / QN, q = u % QN;
+                f32x4 lo[NW], hi[NW];
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    lo[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q));
+                    hi[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q + 1));
+                }
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        s0[i] += lo[w][i];
+                        s1[i] += hi[w][i];
+                    }
+                }
+                half4 h0, h1;
+                if (plain) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v0 = s0[i] * alpha, v1 = s1[i] * alpha;
+                        h0[i] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
+                        h1[i] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
+                    }
+                } else {
+                    h0 = epilogue4<ACT>(s0, alpha, bvs[j][0]);
+                    h1 = epilogue4<ACT>(s1, alpha, bvs[j][1]);
+                }
+                const int m = m0 + mr, n = n0 + 8 * q;
+                const uint32_t off =
+                    ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+                const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{w0[0], w0[1], w1[0], w1[1]}, rc, off, 0, 0);
+            }
+        });
+    }
+};
+
 template <int BM, int BN, int STAGES>
 __global__ void __launch_bounds__(256)
 gemm_scale_relu_ksplit_kernel(Problem p)
 {
     using T = KsCfg<BM, BN, STAGES>;
-    constexpr int BK = T::BK, NW = T::NW, CHA = T::CHA, CHN = T::CHN, TM = T::TM, TN = T::TN, NB = T::NB;
+    constexpr int BK = T::BK, NW = T::NW, CHA = T::CHA, CHN = T::CHN, TM = T::TM, TN = T::TN;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
@@ -215,83 +328,17 @@ gemm_scale_relu_ksplit_kernel(Problem p)
     }
 
     // ---- sum the four partial tiles through LDS ---------------------------------
-    // The variant's bias values of this wave's output units are requested
-    // first, so their latency overlaps the reduction.
-    const bool plain = plain_epilogue(p);
-    f32x4 bvs[NB];
-    {
-        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const bool load = !plain && p.bias != nullptr;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int u = j * NW + wave;
-            const int blk = u >> 2, g = u & 3;
-            const int n = n0 + (blk / TM) * 32 + 8 * g + 4 * (int)fhi;
-            bvs[j] = load ? bias4(rbias, n) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    }
+    // The variant's bias values are requested first, so their latency
+    // overlaps the barrier and the partial-tile writes.
+    using Sum = KsSum<BM, BN, NW, T::NT>;
+    static_assert(Sum::BYTES <= T::LDS_BYTES, "partial tiles fit in LDS");
+    f32x4 bvs[Sum::NU][2];
+    Sum::load_bias(p, tid, n0, bvs);
     wait_vmcnt<0>();
     lds_barrier();  // every wave is done with the operand buffers
-    // slot (w, blk, g): 64 lanes x 16 bytes, lane-contiguous
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int slot = (wave * NB + a * TM + b) * 4 + g;
-                const f32x16 av = acc[a][b];
-                f32x4 v;
-                if (g == 0) v = __builtin_shufflevector(av, av, 0, 1, 2, 3);
-                else if (g == 1) v = __builtin_shufflevector(av, av, 4, 5, 6, 7);
-                else if (g == 2) v = __builtin_shufflevector(av, av, 8, 9, 10, 11);
-                else v = __builtin_shufflevector(av, av, 12, 13, 14, 15);
-                *(f32x4*)(smem + slot * 1024 + lane * 16) = v;
-            }
+    Sum::write(smem, acc, wave, lane);
     lds_barrier();
-
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
-    const float alpha = p.alpha;
-    // unit u = blk*4 + g goes to wave u % 4.  All of this wave's partial
-    // reads are issued before any sum, so their latencies overlap.
-    f32x4 part[NB][NW];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int u = j * NW + wave;
-        const int blk = u >> 2, g = u & 3;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) part[j][w] = *(const f32x4*)(smem + ((w * NB + blk) * 4 + g) * 1024 + lane * 16);
-    }
-    with_activation(p.act, [&](auto act_tag) {
-        constexpr int ACT = decltype(act_tag)::value;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int u = j * NW + wave;
-            const int blk = u >> 2, g = u & 3;
-            const int a = blk / TM, b = blk % TM;
-            float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] += part[j][w][i];
-            }
-            const int m = m0 + b * 32 + (int)frow;
-            const int n = n0 + a * 32 + 8 * g + 4 * (int)fhi;
-            half4 hv;
-            if (plain) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = s[i] * alpha;
-                    hv[i] = (_Float16)(v > 0.0f ? v : 0.0f);
-                }
-            } else {
-                const f32x4 sv = {s[0], s[1], s[2], s[3]};
-                hv = epilogue4<ACT>(sv, alpha, bvs[j]);
-            }
-            const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), rc, off, 0, 0);
-        }
-    });
+    Sum::sum_store(p, smem, tid, m0, n0, bvs);
 }
 
 }  // namespace gsr
