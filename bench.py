@@ -216,10 +216,7 @@ def main(argv=None) -> int:
     import tiled_dense_gemm_scale_amd as gsr
     from tiled_dense_gemm_scale_amd import workloads as W
 
-    if args.workload == W.SKINNY.name:
-        w = W.SKINNY
-    else:
-        w = W.WORKLOADS[args.workload]
+    w = W.by_name(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)

@@ -59,6 +59,18 @@ def test_skinny_full(gsr, orc):
     PT.assert_parity(w.name, got, ref)
 
 
+def test_column_shard_full(gsr, orc):
+    """One GPU's column shard of the LLM-MLP layer under 8-way column
+    parallelism (4097 x 1376 x 4096, ragged M and N against 256-wide tiles),
+    every output, in the selector's launch."""
+    w = W.COLSHARD8
+    a, b = W.workload_inputs(w)
+    say(f"[gpu] {w.name} {w.M}x{w.N}x{w.K} alpha={w.alpha} selector")
+    got = PT.run_gpu(a, b, w.alpha)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), w.alpha)
+    PT.assert_parity(w.name, got, ref)
+
+
 @pytest.mark.parametrize("name", ["square_4096", "llm_mlp_4097x11008x4096", "square_16384"])
 def test_workload_sampled(gsr, orc, name):
     w = W.WORKLOADS[name]

@@ -45,11 +45,8 @@ GROUPS = (1, 2, 4, 8, 16)
 
 def parse_shape(text: str) -> Tuple[str, int, int, int, float, float]:
     """(name, M, N, K, alpha, b_std) for a workload name or MxNxK."""
-    if text in W.WORKLOADS:
-        w = W.WORKLOADS[text]
-        return w.name, w.M, w.N, w.K, w.alpha, w.b_std
-    if text == W.SKINNY.name:
-        w = W.SKINNY
+    if text in W.WORKLOADS or text in W.EXTRA:
+        w = W.by_name(text)
         return w.name, w.M, w.N, w.K, w.alpha, w.b_std
     m, n, k = (int(v) for v in text.lower().split("x"))
     return text, m, n, k, 0.5, 1.0

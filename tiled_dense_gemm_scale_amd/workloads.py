@@ -65,6 +65,25 @@ WORKLOAD_ORDER = ["square_256", "square_1024", "square_4096",
 SKINNY = Workload("skinny_16x11008x4096", 16, 11008, 4096, 1.0, 4096 ** -0.5, False,
                   "decode batch of 16 tokens against the 11008x4096 MLP weights")
 
+# One GPU's share of the LLM-MLP up-projection when its columns are split over
+# 8 GPUs (column parallelism: each GPU holds 11008/8 = 1376 columns of B and
+# the whole A, and no partial sums are exchanged).
+COLSHARD8 = Workload("llm_mlp_colshard8_4097x1376x4096", 4097, 1376, 4096, 1.0, 4096 ** -0.5, False,
+                     "one GPU's column shard of the LLM-MLP up-projection split over 8 GPUs "
+                     "(N = 11008/8), A ~ N(0,1), B ~ N(0,1/K), alpha=1.0")
+
+# Shapes timed and tested besides the five workloads above.
+EXTRA: Dict[str, Workload] = {w.name: w for w in [SKINNY, COLSHARD8]}
+
+
+def by_name(name: str) -> Workload:
+    """A workload of either registry by name."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in EXTRA:
+        return EXTRA[name]
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS) + sorted(EXTRA)}")
+
 
 def normal_inputs(M: int, N: int, K: int, seed: int = 0, b_std: float = 1.0
                   ) -> Tuple[torch.Tensor, torch.Tensor]:
