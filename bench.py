@@ -200,6 +200,9 @@ def main(argv=None) -> int:
     ap.add_argument("--zero-input", action="store_true",
                     help="also time the same kernel on all-zero inputs (runs the timed kernel again, "
                          "so leave it off when profiling per-kernel averages)")
+    ap.add_argument("--inputs", choices=["normal", "zeros"], default="normal",
+                    help="zeros: run everything, the timed region included, on all-zero A and B (a study of "
+                         "the data-dependent engine clock under rocprofv3 counters; not the workload's number)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -225,6 +228,9 @@ def main(argv=None) -> int:
     log(f"[bench] workload {w.name}: {w.note}")
 
     a_cpu, b_cpu = W.workload_inputs(w)
+    if args.inputs == "zeros":
+        a_cpu, b_cpu = torch.zeros_like(a_cpu), torch.zeros_like(b_cpu)
+        log("[bench] inputs: all zeros (clock study)")
     a = a_cpu.to(dev)
     b = b_cpu.to(dev)
     c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
@@ -404,7 +410,8 @@ def main(argv=None) -> int:
         "config": {
             "workload": w.name,
             "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
-            "inputs": f"seed 0 randn fp32 -> fp16, A then B, B std {w.b_std:g}",
+            "inputs": (f"seed 0 randn fp32 -> fp16, A then B, B std {w.b_std:g}" if args.inputs == "normal"
+                       else "all zeros (clock study, not the workload's number)"),
             "launch": args.launch,
             "epilogue": args.epilogue,
             "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n", "group_m",
