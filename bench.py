@@ -59,6 +59,27 @@ def load_traffic(workload: str, flops: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def roofline_of(w, ms: float, traffic):
+    """The roofline object of one launch taking `ms` milliseconds.  The bound
+    follows the workload's arithmetic intensity against the ridge point of the
+    two published peaks (2516.6 TFLOP/s / 8 TB/s = 315 FLOP/B): above it the
+    algorithmic FLOP per launch over the time against the MFMA peak, below it
+    the algorithmic bytes 2(MK+KN+MN) over the time against the HBM peak."""
+    ridge = PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if w.flops / w.algorithmic_bytes >= ridge:
+        achieved, peak, unit, bound = w.flops / (ms * 1e-3) / 1e12, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = w.algorithmic_bytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    return {
+        "bound": bound,
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic,
+    }
+
+
 def device_info(index: int) -> dict:
     """CU count and maximum engine clock as the HIP runtime reports them."""
     import ctypes
@@ -372,22 +393,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 2} bytes read, {n * 2} bytes written")
 
-    traffic = load_traffic(w.name, w.flops)
-    # The bound follows the workload's arithmetic intensity against the ridge
-    # point of the two published peaks (2516.6 TFLOP/s / 8 TB/s = 315 FLOP/B).
-    ridge = PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if w.flops / w.algorithmic_bytes >= ridge:
-        achieved, peak, unit, bound = tflops, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
-    else:
-        achieved, peak, unit, bound = w.algorithmic_bytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
-    roofline = {
-        "bound": bound,
-        "achieved": round(achieved, 3),
-        "peak": peak,
-        "unit": unit,
-        "frac": round(achieved / peak, 4),
-        "traffic": traffic,
-    }
+    roofline = roofline_of(w, ms, load_traffic(w.name, w.flops))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)")
