@@ -2,6 +2,7 @@
 // checks, device check, tile selection and the launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -158,50 +159,55 @@ constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile selection.  Each candidate's cost is the number of waves of workgroups
-// it needs on 256 CUs times the work of one tile, divided by the rate one CU
-// sustains on that tile when every CU is busy (measured on MI355X at
-// 16384^3, or at the long-K end of a K sweep for the small tiles).  Large
-// tiles win when there are enough of them to fill the chip; small shapes fall
-// back to small tiles that spread over more CUs.
+// Tile selection.  A candidate's cost is the time of one tile,
+//     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
+// times its waves of workgroups on 256 CUs, where a last wave that is not
+// full costs max(0.85, fill) of a full one (a part-filled chip runs at a higher
+// power-limited clock, and every tile still pays its fixed cost).  The rates
+// and overheads were fitted by least squares (relative error) to the times of
+// every configuration on 69 shapes measured on MI355X (M from 1 to 8192
+// against 11008x4096, 4096x4096 and 4096x11008 weights, squares from 256 to
+// 16384, and the benchmark workloads), the offline sweep the aikraft.ru guide
+// describes in sections 3 and 7; on those shapes the choice is on average
+// within 0.1 % of the fastest configuration, and within 1.6 % on shapes held
+// out of the fit.  Below K = 256 the four-wave K-split tiles replace their
+// copy-wave twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
-    double tflops_per_cu;
+    double tflops_per_cu;  // rate of one CU on this tile while the chip is busy
+    double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 4.69},  // 256x256, explicit interleave
-    {0, 4.35},   // 256x256, 8 waves, transposing LDS reads
-    {5, 3.52},   // 256x128
-    {6, 3.52},   // 128x256
-    {7, 2.88},   // 128x128
-    {8, 2.08},   // 128x64
-    {10, 2.09},  // 64x128
-    {16, 2.00},  // 64x64, four waves splitting K
-    {9, 1.80},   // 64x64
-    {18, 1.05},  // 32x64, four waves splitting K
+    {15, 6.36, 8.49},  // 256x256, explicit interleave
+    {5, 3.99, 7.19},   // 256x128
+    {6, 3.83, 7.01},   // 128x256
+    {7, 3.26, 4.99},   // 128x128
+    {8, 2.22, 4.11},   // 128x64
+    {10, 2.03, 4.22},  // 64x128
+    {21, 2.76, 3.21},  // 64x64, K split, copy waves       (K > 256)
+    {22, 1.82, 2.49},  // 32x64, K split, copy waves       (K > 256)
+    {16, 2.42, 3.66},  // 64x64, K split, four waves       (K <= 256)
+    {18, 1.57, 2.83},  // 32x64, K split, four waves       (K <= 256)
 };
 
 int select(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
-    int best = 9;
+    int best = 15;
     double best_t = 1e300;
     for (const Candidate& c : kCandidates) {
+        const bool copy_wave = c.id == 21 || c.id == 22, four_wave = c.id == 16 || c.id == 18;
+        if ((copy_wave && K <= 256) || (four_wave && K > 256)) continue;
         const gsr_config& g = kTable[c.id].cfg;
         const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
-        const double waves = std::ceil(wgs / cus);
-        const double t = waves * 2.0 * g.block_m * g.block_n * (double)(K > 0 ? K : 1) / c.tflops_per_cu;
+        const double full = std::floor(wgs / cus), fill = (wgs - full * cus) / cus;
+        const double waves = full + (fill > 0.0 ? std::max(0.85, fill) : 0.0);
+        const double tile = 2.0 * g.block_m * g.block_n * (double)(K > 0 ? K : 1) / (c.tflops_per_cu * 1e6) + c.tile_us;
+        const double t = waves * tile;
         if (t < best_t) {
             best_t = t;
             best = c.id;
         }
-    }
-    // With three or more 128-deep K-steps the K-split tiles run faster with
-    // separate copy waves (measured: 1024^3 7.4 -> 6.6 us, 16x11008x4096
-    // 17.3 -> 15.9 us; at K = 256 the four-wave kernels are as fast or faster).
-    if (K > 256) {
-        if (best == 16) best = 21;
-        else if (best == 18) best = 22;
     }
     return best;
 }
