@@ -165,12 +165,13 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // full costs max(0.85, fill) of a full one (a part-filled chip runs at a higher
 // power-limited clock, and every tile still pays its fixed cost).  The rates
 // and overheads were fitted by least squares (relative error) to the times of
-// every configuration on 69 shapes measured on MI355X (M from 1 to 8192
+// every configuration on 60 shapes measured on MI355X (M from 1 to 8192
 // against 11008x4096, 4096x4096 and 4096x11008 weights, squares from 256 to
 // 16384, and the benchmark workloads), the offline sweep the aikraft.ru guide
-// describes in sections 3 and 7; on those shapes the choice is on average
-// within 0.1 % of the fastest configuration, and within 1.6 % on shapes held
-// out of the fit.  Below K = 256 the four-wave K-split tiles replace their
+// describes in sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
+// tuning/mi355x_config_times.csv reproduces this table); on those shapes the
+// choice is on average within 0.1 % of the fastest configuration, and within
+// 1.6 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
 // copy-wave twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
@@ -185,7 +186,7 @@ const Candidate kCandidates[] = {
     {8, 2.22, 4.11},   // 128x64
     {10, 2.03, 4.22},  // 64x128
     {21, 2.76, 3.21},  // 64x64, K split, copy waves       (K > 256)
-    {22, 1.82, 2.49},  // 32x64, K split, copy waves       (K > 256)
+    {22, 1.81, 2.49},  // 32x64, K split, copy waves       (K > 256)
     {16, 2.42, 3.66},  // 64x64, K split, four waves       (K <= 256)
     {18, 1.57, 2.83},  // 32x64, K split, four waves       (K <= 256)
 };
