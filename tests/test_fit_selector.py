@@ -21,7 +21,7 @@ def test_fit_recovers_a_known_model():
     times = {}
     for M in (16, 200, 1000, 4100):
         for N in (512, 3000, 11008):
-            for K in (128, 1024, 4096):
+            for K in (128, 256, 1024, 4096):
                 times[(M, N, K)] = {cid: F.waves(F.workgroups(tiles[cid], M, N), a, pmin)
                                     * (2.0 * tiles[cid][0] * tiles[cid][1] * K / (r * 1e6) + e)
                                     for cid, (r, e) in truth.items() if cid in F.candidates(K)}
