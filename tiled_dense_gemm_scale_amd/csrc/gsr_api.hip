@@ -19,6 +19,7 @@
 #include "gsr_ksplit.hpp"
 #include "gsr_dual.hpp"
 #include "gsr_kspec.hpp"
+#include "gsr_interleave_h.hpp"
 
 namespace {
 
@@ -53,6 +54,12 @@ hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
 hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ilvh(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilvh_kernel, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -154,6 +161,8 @@ const Entry kTable[] = {
     // K split with separate copy waves (eight waves per workgroup), two steps ahead
     GSR_KSPEC(21, 64, 64, 4, 2, 4),
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
+    // explicit interleave at half height, 4 waves of 64x128; stages = 1 as for GSR_BT
+    Entry{{23, 128, 256, 64, 2, 2, 1, 4, 1, gsr::IlvHCfg::LDS_BYTES}, launch_ilvh, launch_staged<128, 256, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -171,7 +180,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // describes in sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
 // choice is on average within 0.1 % of the fastest configuration, and within
-// 1.6 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
+// 1.7 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
 // copy-wave twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
@@ -179,16 +188,17 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 6.36, 8.49},  // 256x256, explicit interleave
-    {5, 3.99, 7.19},   // 256x128
-    {6, 3.83, 7.01},   // 128x256
-    {7, 3.26, 4.99},   // 128x128
-    {8, 2.22, 4.11},   // 128x64
-    {10, 2.03, 4.22},  // 64x128
-    {21, 2.76, 3.21},  // 64x64, K split, copy waves       (K > 256)
-    {22, 1.81, 2.49},  // 32x64, K split, copy waves       (K > 256)
-    {16, 2.42, 3.66},  // 64x64, K split, four waves       (K <= 256)
-    {18, 1.57, 2.83},  // 32x64, K split, four waves       (K <= 256)
+    {15, 6.32, 8.32},  // 256x256, explicit interleave
+    {23, 4.62, 5.67},  // 128x256, explicit interleave
+    {5, 3.95, 7.09},   // 256x128
+    {6, 3.80, 6.92},   // 128x256
+    {7, 3.22, 4.96},   // 128x128
+    {10, 2.03, 4.12},  // 64x128
+    {8, 2.22, 4.06},   // 128x64
+    {21, 2.72, 3.28},  // 64x64, K split, copy waves       (K > 256)
+    {22, 1.80, 2.49},  // 32x64, K split, copy waves       (K > 256)
+    {16, 2.38, 3.63},  // 64x64, K split, four waves       (K <= 256)
+    {18, 1.57, 2.84},  // 32x64, K split, four waves       (K <= 256)
 };
 
 int select(int64_t M, int64_t N, int64_t K)

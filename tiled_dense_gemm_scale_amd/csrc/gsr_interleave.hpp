@@ -75,21 +75,22 @@ __device__ __forceinline__ void wait_vmcnt_b(u32x4 (&r)[8])
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// The epilogue of the 256x256 kernels: scale, ReLU (or the variant: scale,
-// bias, activation) and round in registers, then pass each wave's 128x128
-// fp16 sub-tile through its own 32 KB of LDS so that the global stores write
+// The epilogue of the interleaved kernels: scale, ReLU (or the variant: scale,
+// bias, activation) and round in registers, then pass each wave's WTM x 128
+// fp16 sub-tile through its own WTM x 256 bytes of LDS so that the global stores write
 // whole 256-byte row segments (16 lanes per row) instead of 16 bytes in each
 // of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at physical
 // chunk c ^ (r % 16).  Called once every wave's copies have been drained.
-__device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&acc)[IlvCfg::TN][IlvCfg::TM],
+template <class T = IlvCfg>
+__device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&acc)[T::TN][T::TM],
                                              uint8_t* smem, int m0, int n0, int wm, int wn, int wave,
                                              uint32_t frow, uint32_t fhi)
 {
-    using T = IlvCfg;
     constexpr int TM = T::TM, TN = T::TN;
     const uint32_t lane = (uint32_t)(threadIdx.x & 63);
     const uint32_t N = (uint32_t)p.N;
     static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
+    static_assert(T::WTN == 128 && T::WTM % 32 == 0, "256-byte staging rows");
     // The variant's bias values for the lane's 16 column groups are requested
     // before the barrier, so their latency overlaps it.
     const bool plain = plain_epilogue(p);
