@@ -14,7 +14,7 @@ API = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc", "gsr_api.hip")
 
 def test_fit_recovers_a_known_model():
     """Times generated from known rates and fixed costs are fitted back."""
-    tiles = {15: (256, 256), 23: (128, 256), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128), 8: (128, 64),
+    tiles = {15: (256, 256), 23: (128, 256), 24: (128, 128), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128), 8: (128, 64),
              21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
     truth = {cid: (1.0 + 0.5 * i, 2.0 + 0.25 * i) for i, cid in enumerate(sorted(tiles))}
     a, pmin = 0.2, 0.6

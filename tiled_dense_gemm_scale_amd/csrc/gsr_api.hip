@@ -20,6 +20,7 @@
 #include "gsr_dual.hpp"
 #include "gsr_kspec.hpp"
 #include "gsr_interleave_h.hpp"
+#include "gsr_interleave_q.hpp"
 
 namespace {
 
@@ -60,6 +61,12 @@ hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 hipError_t launch_ilvh(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(gsr::gemm_scale_relu_ilvh_kernel, dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilvq_kernel, dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -163,6 +170,8 @@ const Entry kTable[] = {
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
     // explicit interleave at half height, 4 waves of 64x128; stages = 1 as for GSR_BT
     Entry{{23, 128, 256, 64, 2, 2, 1, 4, 1, gsr::IlvHCfg::LDS_BYTES}, launch_ilvh, launch_staged<128, 256, 64, 2, 2, false>},
+    // explicit interleave at a quarter of 256x256, 4 waves of 64x64
+    Entry{{24, 128, 128, 64, 2, 2, 1, 4, 1, gsr::IlvQCfg::LDS_BYTES}, launch_ilvq, launch_staged<128, 128, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -180,7 +189,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // describes in sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
 // choice is on average within 0.1 % of the fastest configuration, and within
-// 1.7 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
+// 1.4 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
 // copy-wave twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
@@ -188,17 +197,18 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 6.32, 8.32},  // 256x256, explicit interleave
-    {23, 4.62, 5.67},  // 128x256, explicit interleave
-    {5, 3.95, 7.09},   // 256x128
-    {6, 3.80, 6.92},   // 128x256
-    {7, 3.22, 4.96},   // 128x128
-    {10, 2.03, 4.12},  // 64x128
-    {8, 2.22, 4.06},   // 128x64
-    {21, 2.72, 3.28},  // 64x64, K split, copy waves       (K > 256)
-    {22, 1.80, 2.49},  // 32x64, K split, copy waves       (K > 256)
-    {16, 2.38, 3.63},  // 64x64, K split, four waves       (K <= 256)
-    {18, 1.57, 2.84},  // 32x64, K split, four waves       (K <= 256)
+    {15, 6.36, 8.44},  // 256x256, explicit interleave
+    {23, 4.65, 5.80},  // 128x256, explicit interleave
+    {24, 3.41, 4.12},  // 128x128, explicit interleave
+    {5, 3.98, 7.15},   // 256x128
+    {6, 3.82, 7.00},   // 128x256
+    {7, 3.24, 5.02},   // 128x128
+    {10, 2.03, 4.19},  // 64x128
+    {8, 2.22, 4.12},   // 128x64
+    {21, 2.75, 3.20},  // 64x64, K split, copy waves       (K > 256)
+    {22, 1.81, 2.50},  // 32x64, K split, copy waves       (K > 256)
+    {16, 2.42, 3.66},  // 64x64, K split, four waves       (K <= 256)
+    {18, 1.57, 2.81},  // 32x64, K split, four waves       (K <= 256)
 };
 
 int select(int64_t M, int64_t N, int64_t K)

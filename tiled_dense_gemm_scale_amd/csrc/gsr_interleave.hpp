@@ -76,11 +76,11 @@ __device__ __forceinline__ void wait_vmcnt_b(u32x4 (&r)[8])
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // The epilogue of the interleaved kernels: scale, ReLU (or the variant: scale,
-// bias, activation) and round in registers, then pass each wave's WTM x 128
-// fp16 sub-tile through its own WTM x 256 bytes of LDS so that the global stores write
-// whole 256-byte row segments (16 lanes per row) instead of 16 bytes in each
-// of 32 rows.  Rows are 256 bytes; 16-byte chunk c of row r sits at physical
-// chunk c ^ (r % 16).  Called once every wave's copies have been drained.
+// bias, activation) and round in registers, then pass each wave's WTM x WTN
+// fp16 sub-tile through its own WTM x 2*WTN bytes of LDS so that the global
+// stores write whole row segments (WTN/8 lanes of 16 bytes per row) instead of
+// 16 bytes in each of 32 rows.  16-byte chunk c of row r sits at physical
+// chunk c ^ (r % (WTN/8)).  Called once every wave's copies have been drained.
 template <class T = IlvCfg>
 __device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&acc)[T::TN][T::TM],
                                              uint8_t* smem, int m0, int n0, int wm, int wn, int wave,
@@ -90,7 +90,8 @@ __device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&ac
     const uint32_t lane = (uint32_t)(threadIdx.x & 63);
     const uint32_t N = (uint32_t)p.N;
     static_assert(T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "epilogue tile fits");
-    static_assert(T::WTN == 128 && T::WTM % 32 == 0, "256-byte staging rows");
+    constexpr uint32_t CPR = T::WTN / 8, RB = T::WTN * 2;  // chunks and bytes per staging row
+    static_assert((T::WTN == 128 || T::WTN == 64) && T::WTM % 32 == 0, "staging rows of 8 or 16 chunks");
     // The variant's bias values for the lane's 16 column groups are requested
     // before the barrier, so their latency overlaps it.
     const bool plain = plain_epilogue(p);
@@ -110,8 +111,8 @@ __device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&ac
     uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
     auto stage4 = [&](int a, int b, int g, half4 h) {
         const uint32_t r = (uint32_t)b * 32u + frow;
-        const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & 15u);
-        *(u32x2*)(ep + r * 256u + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
+        const uint32_t c = ((uint32_t)(4 * a + g)) ^ (r & (CPR - 1u));
+        *(u32x2*)(ep + r * RB + c * 16u + fhi * 8u) = __builtin_bit_cast(u32x2, h);
     };
     if (plain) {
 #pragma unroll
@@ -155,12 +156,13 @@ __device__ __forceinline__ void ilv_epilogue(const Problem& p, const f32x16 (&ac
     // wave's accesses in order, so only the compiler must not move them.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
-    const uint32_t sc = (uint32_t)lane & 15u;
+    constexpr uint32_t RPI = 64u / CPR;  // rows per store instruction
+    const uint32_t sc = (uint32_t)lane & (CPR - 1u);
     const int n = n0 + wn * T::WTN + 8 * (int)sc;
 #pragma unroll
-    for (int j = 0; j < T::WTM / 4; ++j) {
-        const uint32_t r = 4u * (uint32_t)j + ((uint32_t)lane >> 4);
-        const u32x4 v = *(const u32x4*)(ep + r * 256u + ((sc ^ (r & 15u)) << 4));
+    for (int j = 0; j < (int)(T::WTM / RPI); ++j) {
+        const uint32_t r = RPI * (uint32_t)j + (uint32_t)lane / CPR;
+        const u32x4 v = *(const u32x4*)(ep + r * RB + ((sc ^ (r & (CPR - 1u))) << 4));
         const int m = m0 + wm * T::WTM + (int)r;
         const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);

@@ -32,7 +32,7 @@ CUS = 256
 Shape = Tuple[int, int, int]
 # the selector's candidates; the copy-wave K-split tiles only for K > 256,
 # their four-wave twins only for K <= 256
-BASE = [15, 23, 5, 6, 7, 10, 8]
+BASE = [15, 23, 24, 5, 6, 7, 10, 8]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
 
