@@ -332,7 +332,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 300; }
+int gsr_version(void) { return 400; }
 
 const char* gsr_status_string(int status)
 {
