@@ -21,6 +21,7 @@
 #include "gsr_kspec.hpp"
 #include "gsr_interleave_h.hpp"
 #include "gsr_interleave_q.hpp"
+#include "gsr_interleave16.hpp"
 
 namespace {
 
@@ -55,6 +56,12 @@ hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
 hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ilv16(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -172,6 +179,8 @@ const Entry kTable[] = {
     Entry{{23, 128, 256, 64, 2, 2, 1, 4, 1, gsr::IlvHCfg::LDS_BYTES}, launch_ilvh, launch_staged<128, 256, 64, 2, 2, false>},
     // explicit interleave at a quarter of 256x256, 4 waves of 64x64
     Entry{{24, 128, 128, 64, 2, 2, 1, 4, 1, gsr::IlvQCfg::LDS_BYTES}, launch_ilvq, launch_staged<128, 128, 64, 2, 2, false>},
+    // config 15's tile and data flow on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave)
+    Entry{{25, 256, 256, 64, 2, 2, 1, 4, 1, gsr::Ilv16Cfg::LDS_BYTES}, launch_ilv16, launch_staged<256, 256, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
