@@ -18,21 +18,22 @@
 // 16-byte chunk of the substep's four (A and B^T are both K-contiguous in
 // LDS, 16-byte chunks XOR-swizzled by row).
 //
-// Operand registers: one X set (an X fragment is refilled for the next
-// substep as soon as its eight MFMAs have issued) and two Y sets (all eight Y
-// fragments are used across the whole substep).  Per substep the reads are:
-// X[7] of the substep itself at slot 0, X[a] of the next substep at slot
-// 8a + 8, Y[b] of the next substep every fourth slot from slot 2 (substep 0)
-// or 4 (substep 1, after the barrier).
+// Operand registers: one set of X[0..6] (an X fragment is refilled for the
+// next substep as soon as its eight MFMAs have issued), two of X[7] and two Y
+// sets (all eight Y fragments are used across the whole substep).  Each
+// substep reads the next substep's operands: X[a] at slot 8a + 8, X[7] at slot
+// 44 (substep 0) or 60 (substep 1), Y[b] every fourth slot from slot 2
+// (substep 0) or 8 (substep 1, after the barrier).  The barrier waits for
+// this wave's LDS operations; the last read before it is 14 slots old.
 //
 // Companions of step t on stage S (SN = S ^ 1):
 //   substep 0, slots 16-31: wait for B(t+1), transpose it in registers;
 //   substep 0, slots 33-47 (odd): write B(t+1)^T into stage SN;
 //   substep 0, slots 49-63 (odd): load B(t+2) into registers;
-//   substep 1, slot 2:   wait for the A(t+1) copies, barrier (publishes
+//   substep 1, slot 6:   wait for the A(t+1) copies, barrier (publishes
 //                        stage SN, frees stage S);
-//   substep 1, slots 3-17 (odd): copy A(t+2) into stage S;
-//   substep 1 reads from slot 4 on come from stage SN (step t+1).
+//   substep 1, slots 7-21 (odd): copy A(t+2) into stage S;
+//   substep 1 reads (from slot 8 on) come from stage SN (step t+1).
 #pragma once
 
 #include <type_traits>
@@ -211,7 +212,8 @@ gemm_scale_relu_ilv16_kernel(Problem p)
 #pragma unroll
         for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    half8 X[FN];      // B^T fragments, refilled one by one
+    half8 X[FN - 1];  // B^T fragments 0..6, refilled one by one
+    half8 X7[2];      // B^T fragment 7, one per substep parity
     half8 Y[2][FM];   // A^T fragments, one set per substep parity
     u32x4 breg[8];    // B block of a future step
     u32x4 bcol[8];    // its transpose
@@ -227,22 +229,27 @@ gemm_scale_relu_ilv16_kernel(Problem p)
     };
     auto read_x = [&](int S, int ks, int a) {
         const uint32_t off = xb[a & 3] ^ (ks ? 64u : 0u);
-        X[a] = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::B_BYTES + (a >> 2) * (64 * BK * 2) + off));
+        const half8 v = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::B_BYTES + (a >> 2) * (64 * BK * 2) + off));
+        if (a == FN - 1) X7[ks] = v;
+        else X[a] = v;
     };
     auto read_y = [&](int S, int ks, int b, half8& dst) {
         const uint32_t off = (xb[b & 3] ^ (ks ? 64u : 0u)) - ydelta;
         dst = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::A_BYTES + (b >> 2) * (64 * BK * 2) + off));
     };
-    // The reads of slot i of a substep: X[7] of this substep (stage S, substep
-    // ks) at slot 0; X[a] of the next substep (stage SR, substep kr) at slot
-    // 8a + 8, as soon as its last MFMA here has issued; Y[b] of the next
-    // substep at slot y0 + 4b, at least 40 slots before its first use.
-    auto reads = [&](int i, int S, int ks, int SR, int kr, half8 (&ynext)[FM], int y0) {
-        if (i == 0) read_x(S, ks, FN - 1);
-        else if ((i & 7) == 0) read_x(SR, kr, (i >> 3) - 1);
+    // The reads of slot i of a substep, all for the next substep (stage SR,
+    // substep kr): X[a] (a < 7) at slot 8a + 8, as soon as its last MFMA here
+    // has issued; X[7] (into the other X7 register) at slot x7; Y[b] at slot
+    // y0 + 4b, at least 30 slots before its first use.
+    auto reads = [&](int i, int SR, int kr, half8 (&ynext)[FM], int y0, int x7) {
+        if ((i & 7) == 0 && i >= 8 && i <= 8 * (FN - 1)) read_x(SR, kr, (i >> 3) - 1);
+        if (i == x7) read_x(SR, kr, FN - 1);
         if (i >= y0 && i < y0 + 4 * FM && ((i - y0) & 3) == 0) read_y(SR, kr, (i - y0) >> 2, ynext[(i - y0) >> 2]);
     };
-    auto mma = [&](int i, const half8 (&ys)[FM]) { mfma16_inplace(acc[i >> 3][i & 7], X[i >> 3], ys[i & 7]); };
+    auto mma = [&](int i, int ks, const half8 (&ys)[FM]) {
+        const int a = i >> 3;
+        mfma16_inplace(acc[a][i & 7], a == FN - 1 ? X7[ks] : X[a], ys[i & 7]);
+    };
 
     auto step = [&](auto stage_tag, int t) {
         constexpr int S = decltype(stage_tag)::value;
@@ -258,8 +265,8 @@ gemm_scale_relu_ilv16_kernel(Problem p)
             const i32x4 rb = b_rsrc(k2);
 #pragma unroll
             for (int i = 0; i < 64; ++i) {
-                mma(i, Y[0]);
-                reads(i, S, 0, S, 1, Y[1], 2);
+                mma(i, 0, Y[0]);
+                reads(i, S, 1, Y[1], 2, 44);
                 if (i == 16) wait_vmcnt_b<T::A_PER>(breg);  // B(t+1) is in; A(t+1) copies may not be
                 if (i >= 16 && i < 32) {
                     // 2 of the 32 byte-permute pairs per slot
@@ -278,13 +285,13 @@ gemm_scale_relu_ilv16_kernel(Problem p)
             const i32x4 ra = a_rsrc(k2);
 #pragma unroll
             for (int i = 0; i < 64; ++i) {
-                mma(i, Y[1]);
-                if (i == 2) {
+                mma(i, 1, Y[1]);
+                if (i == 6) {
                     wait_vmcnt<T::B_LOADS>();  // A(t+1) copies are in; B(t+2) loads may not be
                     lds_barrier();
                 }
-                reads(i, S, 1, SN, 0, Y[0], 4);
-                if (i >= 3 && i < 18 && (i & 1)) copy_a(S, (i - 3) >> 1, kleft2, ra);
+                reads(i, SN, 0, Y[0], 8, 60);
+                if (i >= 7 && i < 22 && (i & 1)) copy_a(S, (i - 7) >> 1, kleft2, ra);
                 sched_fence();
             }
         }
@@ -311,9 +318,9 @@ gemm_scale_relu_ilv16_kernel(Problem p)
 #pragma unroll
         for (int i = 0; i < T::A_PER; ++i) copy_a(1, i, kleft1, ra1);
         lds_barrier();
-        // substep-0 operands of step 0 except X[7], which slot 0 reads
+        // substep-0 operands of step 0
 #pragma unroll
-        for (int a = 0; a < FN - 1; ++a) read_x(0, 0, a);
+        for (int a = 0; a < FN; ++a) read_x(0, 0, a);
 #pragma unroll
         for (int b = 0; b < FM; ++b) read_y(0, 0, b, Y[0][b]);
     }
