@@ -15,22 +15,31 @@ API = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc", "gsr_api.hip")
 def test_fit_recovers_a_known_model():
     """Times generated from known rates and fixed costs are fitted back."""
     tiles = {15: (256, 256), 23: (128, 256), 24: (128, 128), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128), 8: (128, 64),
-             21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
+             25: (256, 256), 21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
     truth = {cid: (1.0 + 0.5 * i, 2.0 + 0.25 * i) for i, cid in enumerate(sorted(tiles))}
-    a, pmin = 0.2, 0.6
+    a, pmin, full = 0.2, 0.6, 96
     times = {}
-    for M in (16, 200, 1000, 4100):
+    for M in (16, 200, 1000, 4100, 8200):
         for N in (512, 3000, 11008):
             for K in (128, 256, 1024, 4096):
                 times[(M, N, K)] = {cid: F.waves(F.workgroups(tiles[cid], M, N), a, pmin)
                                     * (2.0 * tiles[cid][0] * tiles[cid][1] * K / (r * 1e6) + e)
-                                    for cid, (r, e) in truth.items() if cid in F.candidates(K)}
-    params = F.fit_params(times, tiles, a, pmin)
+                                    for cid, (r, e) in truth.items() if cid in F.candidates(M, N, K, full)}
+    params = F.fit_params(times, tiles, a, pmin, full)
     for cid, (r, e) in truth.items():
         assert params[cid][0] == pytest.approx(r, rel=1e-6)
         assert params[cid][1] == pytest.approx(e, rel=1e-6, abs=1e-9)
-    mean, worst = F.regret(times, tiles, params, a, pmin)
+    mean, worst = F.regret(times, tiles, params, a, pmin, full)
     assert mean == pytest.approx(1.0) and worst == pytest.approx(1.0)
+
+
+def test_full_chip_rule_swaps_the_256_tile_kernel():
+    assert 15 in F.candidates(1024, 4096, 4096, 160) and 25 not in F.candidates(1024, 4096, 4096, 160)
+    assert 25 in F.candidates(4096, 4096, 4096, 160) and 15 not in F.candidates(4096, 4096, 4096, 160)
+    assert F.workgroups((256, 256), 2560, 4096) == 160 and 25 in F.candidates(2560, 4096, 4096, 160)
+    assert 15 in F.candidates(2304, 4096, 4096, 160)  # 9 x 16 = 144 tiles
+    assert 25 in F.candidates(2305, 4000, 4096, 160)  # a ragged tenth tile row: 10 x 16 = 160 tiles
+    assert F.candidates(16, 11008, 256, 160)[-2:] == F.FOUR_WAVE and F.candidates(16, 11008, 257, 160)[-2:] == F.COPY_WAVE
 
 
 def test_waves_price_a_partial_last_wave():
@@ -45,7 +54,7 @@ def test_selector_table_is_the_fit_of_the_committed_measurements():
     """The constants in select() are what the fit of the committed times gives."""
     times, tiles = F.load(CSV)
     assert len(times) >= 50
-    mean, worst, a, pmin, params = F.fit(times, tiles)
+    mean, worst, a, pmin, full, params = F.fit(times, tiles)
     src = open(API).read()
     table = src[src.index("const Candidate kCandidates[]"):]
     table = table[: table.index("};")]
@@ -55,17 +64,23 @@ def test_selector_table_is_the_fit_of_the_committed_measurements():
     for cid, (rate, tile_us) in rows.items():
         assert rate == pytest.approx(params[cid][0], abs=0.006), cid
         assert tile_us == pytest.approx(params[cid][1], abs=0.006), cid
-    assert "std::max(0.85, fill)" in src and a == pytest.approx(0.0) and pmin == pytest.approx(0.85)
+    consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
+    assert float(consts.group(1)) == pytest.approx(pmin) and float(consts.group(2)) == pytest.approx(a)
+    assert int(re.search(r"kFullChipTiles = (\d+);", src).group(1)) == full
     assert mean < 1.005 and worst < 1.05
 
 
 def test_library_selector_matches_the_model(native):
     """select() in the library makes the model's choice on every measured shape."""
     times, tiles = F.load(CSV)
-    mean, worst, a, pmin, params = F.fit(times, tiles, a_grid=np.array([0.0]), p_grid=np.array([0.85]))
+    src = open(API).read()
+    consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
+    full = int(re.search(r"kFullChipTiles = (\d+);", src).group(1))
+    mean, worst, a, pmin, full, params = F.fit(times, tiles, a_grid=np.array([float(consts.group(2))]),
+                                               p_grid=np.array([float(consts.group(1))]), full_grid=(full,))
     disagree = []
     for (M, N, K), t in times.items():
-        want = F.choose(params, tiles, M, N, K, a, pmin)
+        want = F.choose(params, tiles, M, N, K, a, pmin, full)
         got = native.select_config(M, N, K)["id"]
         if got != want:
             disagree.append(((M, N, K), got, want))

@@ -189,49 +189,60 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.85, fill) of a full one (a part-filled chip runs at a higher
-// power-limited clock, and every tile still pays its fixed cost).  The rates
-// and overheads were fitted by least squares (relative error) to the times of
-// every configuration on 60 shapes measured on MI355X (M from 1 to 8192
-// against 11008x4096, 4096x4096 and 4096x11008 weights, squares from 256 to
-// 16384, and the benchmark workloads), the offline sweep the aikraft.ru guide
-// describes in sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
+// full costs max(0.30, 0.5 + 0.5 * fill) of a full one (a part-filled chip
+// runs at a higher power-limited clock, but every tile still pays its fixed
+// cost).  The 256x256 tile has two kernels: config 15 (32x32x16 MFMAs, the
+// higher issue efficiency) and config 25 (16x16x32 MFMAs, the higher engine
+// clock on random data once the power limit binds); config 25 takes config
+// 15's place when the 256x256 grid has at least 160 workgroups.  The rates,
+// overheads, the partial-wave form and the 160 were fitted (least squares in
+// relative error for the rates, then the grid point whose choices come
+// closest to the fastest configuration) to the times of every configuration
+// on 60 shapes measured on one MI355X (M from 1 to 8192 against 11008x4096,
+// 4096x4096 and 4096x11008 weights, squares from 256 to 16384, and the
+// benchmark workloads), the offline sweep the aikraft.ru guide describes in
+// sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
-// choice is on average within 0.1 % of the fastest configuration, and within
-// 1.4 % on shapes held out of the fit.  Below K = 256 the four-wave K-split tiles replace their
-// copy-wave twins (at two K-steps the copy waves have nothing to run ahead of).
+// choice is on average within 0.1 % of the fastest configuration.  Below
+// K = 256 the four-wave K-split tiles replace their copy-wave twins (at two
+// K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
     double tflops_per_cu;  // rate of one CU on this tile while the chip is busy
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 6.36, 8.44},  // 256x256, explicit interleave
-    {23, 4.65, 5.80},  // 128x256, explicit interleave
-    {24, 3.41, 4.12},  // 128x128, explicit interleave
-    {5, 3.98, 7.15},   // 256x128
-    {6, 3.82, 7.00},   // 128x256
-    {7, 3.24, 5.02},   // 128x128
-    {10, 2.03, 4.19},  // 64x128
-    {8, 2.22, 4.12},   // 128x64
-    {21, 2.75, 3.20},  // 64x64, K split, copy waves       (K > 256)
-    {22, 1.81, 2.50},  // 32x64, K split, copy waves       (K > 256)
-    {16, 2.42, 3.66},  // 64x64, K split, four waves       (K <= 256)
-    {18, 1.57, 2.81},  // 32x64, K split, four waves       (K <= 256)
+    {15, 5.00, 17.20},  // 256x256, explicit interleave, 32x32x16 (grids below 160 tiles)
+    {23, 4.02, 11.86},  // 128x256, explicit interleave
+    {24, 3.19, 7.91},   // 128x128, explicit interleave
+    {5, 3.61, 14.89},   // 256x128
+    {6, 3.42, 14.77},   // 128x256
+    {7, 3.08, 9.41},    // 128x128
+    {10, 2.07, 7.36},   // 64x128
+    {8, 2.25, 6.91},    // 128x64
+    {25, 4.95, 5.19},   // 256x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
+    {21, 2.65, 3.84},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.79, 2.82},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.37, 4.52},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.60, 3.37},   // 32x64, K split, four waves       (K <= 256)
 };
+constexpr double kPartMin = 0.30, kPartA = 0.50;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr int64_t kFullChipTiles = 160;           // config 25 instead of config 15 from this many 256x256 tiles
 
 int select(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
-    int best = 15;
+    const bool full_chip = cdiv(M, 256) * cdiv(N, 256) >= kFullChipTiles;
+    int best = full_chip ? 25 : 15;
     double best_t = 1e300;
     for (const Candidate& c : kCandidates) {
         const bool copy_wave = c.id == 21 || c.id == 22, four_wave = c.id == 16 || c.id == 18;
         if ((copy_wave && K <= 256) || (four_wave && K > 256)) continue;
+        if ((c.id == 15 && full_chip) || (c.id == 25 && !full_chip)) continue;
         const gsr_config& g = kTable[c.id].cfg;
         const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
         const double full = std::floor(wgs / cus), fill = (wgs - full * cus) / cus;
-        const double waves = full + (fill > 0.0 ? std::max(0.85, fill) : 0.0);
+        const double waves = full + (fill > 0.0 ? std::max(kPartMin, kPartA + (1.0 - kPartA) * fill) : 0.0);
         const double tile = 2.0 * g.block_m * g.block_n * (double)(K > 0 ? K : 1) / (c.tflops_per_cu * 1e6) + c.tile_us;
         const double t = waves * tile;
         if (t < best_t) {
@@ -341,7 +352,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 400; }
+int gsr_version(void) { return 500; }
 
 const char* gsr_status_string(int status)
 {

@@ -6,10 +6,14 @@ The selector in csrc/gsr_api.hip prices a candidate tile bm x bn as
 
 with wgs = ceil(M / bm) * ceil(N / bn) workgroups on 256 CUs and
 waves(wgs) = full waves + (a part-filled last wave: max(pmin, a + (1 - a) * fill)).
-This module fits `rate` (TFLOP/s per CU) and `tile_us` per configuration by
-least squares in relative error, for each (a, pmin) on a grid, and keeps the
-pair whose choices come closest to the fastest measured configuration (mean
-log ratio).  Input: the CSV written from a `tune.py --top 0` report
+The 256x256 tile has two kernels: config 15 (32x32x16 MFMAs, the higher issue
+efficiency) and config 25 (16x16x32 MFMAs, the higher engine clock once enough
+CUs run for the power limit to bind); config 25 stands in for config 15 when
+the 256x256 grid has at least `full` workgroups.  This module fits `rate`
+(TFLOP/s per CU) and `tile_us` per configuration by least squares in relative
+error on the shapes where it is a candidate, for each (a, pmin, full) on a
+grid, and keeps the triple whose choices come closest to the fastest measured
+configuration (mean log ratio).  Input: the CSV written from a `tune.py --top 0` report
 (tuning/mi355x_config_times.csv) or such a JSON report itself.
 
     python -m tiled_dense_gemm_scale_amd.fit_selector tuning/mi355x_config_times.csv
@@ -35,10 +39,14 @@ Shape = Tuple[int, int, int]
 BASE = [15, 23, 24, 5, 6, 7, 10, 8]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
+FULL_CHIP = 25  # stands in for config 15 on grids of at least `full` 256x256 tiles
+ALL = BASE + [FULL_CHIP] + COPY_WAVE + FOUR_WAVE
+FULL_GRID = (64, 96, 128, 160, 192, 224, 256, 320)
 
 
-def candidates(K: int) -> List[int]:
-    return BASE + (COPY_WAVE if K > 256 else FOUR_WAVE)
+def candidates(M: int, N: int, K: int, full: int) -> List[int]:
+    base = BASE if workgroups((256, 256), M, N) < full else [FULL_CHIP] + BASE[1:]
+    return base + (COPY_WAVE if K > 256 else FOUR_WAVE)
 
 
 def load(path: str) -> Tuple[Dict[Shape, Dict[int, float]], Dict[int, Tuple[int, int]]]:
@@ -73,14 +81,17 @@ def workgroups(tile: Tuple[int, int], M: int, N: int) -> int:
     return -(-M // tile[0]) * -(-N // tile[1])
 
 
-def fit_params(times, tiles, a: float, pmin: float) -> Dict[int, Tuple[float, float]]:
+def fit_params(times, tiles, a: float, pmin: float, full: int) -> Dict[int, Tuple[float, float]]:
     """(rate, tile_us) per candidate: least squares of t ~ w * (flops/rate + e),
-    rows scaled by 1/t (relative error)."""
+    rows scaled by 1/t (relative error); configs 15 and 25 on the shapes where
+    the full-chip rule makes them candidates."""
     out = {}
-    for cid in BASE + COPY_WAVE + FOUR_WAVE:
+    for cid in ALL:
         X, y = [], []
         for (M, N, K), t in times.items():
             if cid not in t:
+                continue
+            if cid in (15, FULL_CHIP) and cid not in candidates(M, N, K, full):
                 continue
             w = waves(workgroups(tiles[cid], M, N), a, pmin)
             X.append([w * 2.0 * tiles[cid][0] * tiles[cid][1] * K / 1e6, w])
@@ -93,9 +104,9 @@ def fit_params(times, tiles, a: float, pmin: float) -> Dict[int, Tuple[float, fl
     return out
 
 
-def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, have=None) -> int:
+def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, full: int, have=None) -> int:
     best, best_t = None, math.inf
-    for cid in candidates(K):
+    for cid in candidates(M, N, K, full):
         if cid not in params or (have is not None and cid not in have):
             continue
         rate, e = params[cid]
@@ -105,27 +116,30 @@ def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, have=No
     return best
 
 
-def regret(times, tiles, params, a, pmin) -> Tuple[float, float]:
+def regret(times, tiles, params, a, pmin, full) -> Tuple[float, float]:
     """(mean, worst) of t[choice] / t[fastest] over the shapes."""
     logs, worst = [], 1.0
     for (M, N, K), t in times.items():
-        c = choose(params, tiles, M, N, K, a, pmin, have=t)
+        c = choose(params, tiles, M, N, K, a, pmin, full, have=t)
         r = t[c] / min(t.values())
         logs.append(math.log(r))
         worst = max(worst, r)
     return math.exp(sum(logs) / len(logs)), worst
 
 
-def fit(times, tiles, a_grid=None, p_grid=None):
+def fit(times, tiles, a_grid=None, p_grid=None, full_grid=None):
+    """(mean, worst, a, pmin, full, params) of the best grid point."""
     a_grid = np.arange(0.0, 0.75, 0.05) if a_grid is None else a_grid
     p_grid = np.arange(0.30, 0.90, 0.05) if p_grid is None else p_grid
+    full_grid = FULL_GRID if full_grid is None else full_grid
     best = None
-    for a in a_grid:
-        for p in p_grid:
-            params = fit_params(times, tiles, float(a), float(p))
-            mean, worst = regret(times, tiles, params, float(a), float(p))
-            if best is None or mean < best[0] - 1e-12:
-                best = (mean, worst, float(a), float(p), params)
+    for full in full_grid:
+        for a in a_grid:
+            for p in p_grid:
+                params = fit_params(times, tiles, float(a), float(p), int(full))
+                mean, worst = regret(times, tiles, params, float(a), float(p), int(full))
+                if best is None or mean < best[0] - 1e-12:
+                    best = (mean, worst, float(a), float(p), int(full), params)
     return best
 
 
@@ -135,9 +149,10 @@ def main(argv=None) -> int:
     ap.add_argument("--holdout-splits", type=int, default=6)
     args = ap.parse_args(argv)
     times, tiles = load(args.times)
-    mean, worst, a, p, params = fit(times, tiles)
-    print(f"# {len(times)} shapes; waves: part-filled last wave costs max({p:.2f}, {a:.2f} + {1 - a:.2f} * fill)")
-    for cid in BASE + COPY_WAVE + FOUR_WAVE:
+    mean, worst, a, p, full, params = fit(times, tiles)
+    print(f"# {len(times)} shapes; waves: part-filled last wave costs max({p:.2f}, {a:.2f} + {1 - a:.2f} * fill);"
+          f" config {FULL_CHIP} for config 15 from {full} 256x256 tiles")
+    for cid in ALL:
         if cid in params:
             bm, bn = tiles[cid]
             print(f"    {{{cid}, {params[cid][0]:.2f}, {params[cid][1]:.2f}}},  // {bm}x{bn}")
@@ -149,8 +164,8 @@ def main(argv=None) -> int:
         rnd.shuffle(ks)
         train = {k: times[k] for k in ks[: len(ks) // 2]}
         test = {k: times[k] for k in ks[len(ks) // 2:]}
-        _, _, a_s, p_s, prm = fit(train, tiles)
-        m, w = regret(test, tiles, prm, a_s, p_s)
+        _, _, a_s, p_s, f_s, prm = fit(train, tiles)
+        m, w = regret(test, tiles, prm, a_s, p_s, f_s)
         print(f"# held-out split {seed}: x{m:.4f} on average, x{w:.3f} at worst")
     return 0
 
