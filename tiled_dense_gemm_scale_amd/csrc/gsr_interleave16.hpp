@@ -28,8 +28,8 @@
 //
 // Companions of step t on stage S (SN = S ^ 1):
 //   substep 0, slots 16-31: wait for B(t+1), transpose it in registers;
-//   substep 0, slots 33-47 (odd): write B(t+1)^T into stage SN;
-//   substep 0, slots 49-63 (odd): load B(t+2) into registers;
+//   substep 0, slots 34-62 (every 4th): write B(t+1)^T into stage SN;
+//   substep 0, slots 35-63 (every 4th): load B(t+2) into registers;
 //   substep 1, slot 6:   wait for the A(t+1) copies, barrier (publishes
 //                        stage SN, frees stage S);
 //   substep 1, slots 7-21 (odd): copy A(t+2) into stage S;
@@ -274,8 +274,8 @@ gemm_scale_relu_ilv16_kernel(Problem p)
                     bcol[2 * d][e] = pack_lo(breg[2 * e][d], breg[2 * e + 1][d]);
                     bcol[2 * d + 1][e] = pack_hi(breg[2 * e][d], breg[2 * e + 1][d]);
                 }
-                if (i >= 33 && i < 48 && (i & 1)) write_bt(SN, (i - 33) >> 1);
-                if (i >= 49 && (i & 1)) breg[(i - 49) >> 1] = load16(rb, b_voff((i - 49) >> 1));
+                if (i >= 34 && (i & 3) == 2) write_bt(SN, (i - 34) >> 2);
+                if (i >= 35 && (i & 3) == 3) breg[(i - 35) >> 2] = load16(rb, b_voff((i - 35) >> 2));
                 sched_fence();
             }
         }
@@ -290,7 +290,7 @@ gemm_scale_relu_ilv16_kernel(Problem p)
                     wait_vmcnt<T::B_LOADS>();  // A(t+1) copies are in; B(t+2) loads may not be
                     lds_barrier();
                 }
-                reads(i, SN, 0, Y[0], 8, 60);
+                reads(i, SN, 0, Y[0], 10, 60);
                 if (i >= 7 && i < 22 && (i & 1)) copy_a(S, (i - 7) >> 1, kleft2, ra);
                 sched_fence();
             }
