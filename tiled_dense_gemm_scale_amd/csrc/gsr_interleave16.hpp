@@ -32,7 +32,7 @@
 //   substep 0, slots 35-63 (every 4th): load B(t+2) into registers;
 //   substep 1, slot 6:   wait for the A(t+1) copies, barrier (publishes
 //                        stage SN, frees stage S);
-//   substep 1, slots 7-21 (odd): copy A(t+2) into stage S;
+//   substep 1, slots 7-35 (every 4th): copy A(t+2) into stage S;
 //   substep 1 reads (from slot 8 on) come from stage SN (step t+1).
 #pragma once
 
@@ -291,7 +291,7 @@ gemm_scale_relu_ilv16_kernel(Problem p)
                     lds_barrier();
                 }
                 reads(i, SN, 0, Y[0], 10, 60);
-                if (i >= 7 && i < 22 && (i & 1)) copy_a(S, (i - 7) >> 1, kleft2, ra);
+                if (i >= 7 && i < 39 && (i & 3) == 3) copy_a(S, (i - 7) >> 2, kleft2, ra);
                 sched_fence();
             }
         }
