@@ -189,7 +189,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.30, 0.5 + 0.5 * fill) of a full one (a part-filled chip
+// full costs max(0.75, 0.4 + 0.6 * fill) of a full one (a part-filled chip
 // runs at a higher power-limited clock, but every tile still pays its fixed
 // cost).  The 256x256 tile has two kernels: config 15 (32x32x16 MFMAs, the
 // higher issue efficiency) and config 25 (16x16x32 MFMAs, the higher engine
@@ -212,21 +212,21 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 5.00, 17.20},  // 256x256, explicit interleave, 32x32x16 (grids below 160 tiles)
-    {23, 4.02, 11.86},  // 128x256, explicit interleave
-    {24, 3.19, 7.91},   // 128x128, explicit interleave
-    {5, 3.61, 14.89},   // 256x128
-    {6, 3.42, 14.77},   // 128x256
-    {7, 3.08, 9.41},    // 128x128
-    {10, 2.07, 7.36},   // 64x128
-    {8, 2.25, 6.91},    // 128x64
-    {25, 4.95, 5.19},   // 256x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
-    {21, 2.65, 3.84},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.79, 2.82},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.37, 4.52},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.60, 3.37},   // 32x64, K split, four waves       (K <= 256)
+    {15, 6.05, 10.45},  // 256x256, explicit interleave, 32x32x16 (grids below 160 tiles)
+    {23, 4.31, 6.93},  // 128x256, explicit interleave
+    {24, 3.27, 5.02},   // 128x128, explicit interleave
+    {5, 3.73, 8.68},   // 256x128
+    {6, 3.59, 8.51},   // 128x256
+    {7, 3.12, 6.07},    // 128x128
+    {10, 2.01, 5.07},   // 64x128
+    {8, 2.20, 4.91},    // 128x64
+    {25, 5.27, 4.27},   // 256x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
+    {21, 2.70, 3.49},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.81, 2.65},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.40, 4.06},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.58, 3.06},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.30, kPartA = 0.50;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr double kPartMin = 0.75, kPartA = 0.40;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 constexpr int64_t kFullChipTiles = 160;           // config 25 instead of config 15 from this many 256x256 tiles
 
 int select(int64_t M, int64_t N, int64_t K)
