@@ -60,7 +60,8 @@ enum gsr_activation {
 /* One compiled tile configuration.  A workgroup of waves_m*waves_n wave64s
  * owns a block_m x block_n tile of C and walks K in steps of block_k through
  * `stages` LDS buffers; each wave owns a (block_m/waves_m) x (block_n/waves_n)
- * sub-tile built from 32x32x16 fp16 MFMAs.  group_m is the number of tile rows
+ * sub-tile built from 32x32x16 fp16 MFMAs (config 25, the same 256x256 tile
+ * as config 15: 16x16x32 fp16 MFMAs).  group_m is the number of tile rows
  * in one group of the grouped launch order, xcd_remap says whether workgroup
  * ids are regrouped so that neighbouring tiles run on the same XCD. */
 typedef struct gsr_config {
