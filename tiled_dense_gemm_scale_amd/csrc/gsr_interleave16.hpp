@@ -7,8 +7,10 @@
 // accumulator layout.  Why: with random fp16 operands the part runs
 // power-limited, and a chip-wide stream of v_mfma_f32_16x16x32_f16 holds a
 // markedly higher engine clock than the same FLOP issued as
-// v_mfma_f32_32x32x16_f16 (measured ~1.95-2.0 vs ~1.5-1.6 GHz), so it finishes
-// the same work sooner even though it issues a little below its nominal rate.
+// v_mfma_f32_32x32x16_f16 (both at their full issue rate: ~1.7-1.8 vs
+// ~1.4-1.5 GHz), so where enough CUs run for that limit to bind it finishes
+// the same work sooner even though its 16-cycle MFMAs leave half the issue
+// shadow for the other instructions of a K-step.
 //
 // Each wave owns 128x128 of the tile as 8 x 8 accumulator blocks of 16x16
 // (four fp32 per lane each, all 256 in AGPRs).  A K-step (BK = 64) is two
@@ -23,8 +25,10 @@
 // sets (all eight Y fragments are used across the whole substep).  Each
 // substep reads the next substep's operands: X[a] at slot 8a + 8, X[7] at slot
 // 44 (substep 0) or 60 (substep 1), Y[b] every fourth slot from slot 2
-// (substep 0) or 8 (substep 1, after the barrier).  The barrier waits for
-// this wave's LDS operations; the last read before it is 14 slots old.
+// (substep 0) or 10 (substep 1, after the barrier).  The barrier waits for
+// this wave's LDS operations: the last read before it is 14 slots old, the
+// last B^T write 8.  Spreading the companions evenly over the slots matters
+// as much as what they are (one MFMA every 16 cycles cannot wait on a burst).
 //
 // Companions of step t on stage S (SN = S ^ 1):
 //   substep 0, slots 16-31: wait for B(t+1), transpose it in registers;
@@ -269,7 +273,7 @@ gemm_scale_relu_ilv16_kernel(Problem p)
                 reads(i, S, 1, Y[1], 2, 44);
                 if (i == 16) wait_vmcnt_b<T::A_PER>(breg);  // B(t+1) is in; A(t+1) copies may not be
                 if (i >= 16 && i < 32) {
-                    // 2 of the 32 byte-permute pairs per slot
+                    // one of the 16 byte-permute pairs (two permutes) per slot
                     const int e = (i - 16) >> 2, d = (i - 16) & 3;
                     bcol[2 * d][e] = pack_lo(breg[2 * e][d], breg[2 * e + 1][d]);
                     bcol[2 * d + 1][e] = pack_hi(breg[2 * e][d], breg[2 * e + 1][d]);
