@@ -47,6 +47,28 @@ def test_largest_operand_under_2gib(gsr, orc, K):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cid", [15, 25])
+def test_largest_operand_under_2gib_256_tiles(gsr, orc, cid):
+    """The same A just under 2^31 bytes through each 256x256 kernel, forced:
+    their per-lane copy offsets are formed from base registers plus strides
+    of 32 and 64 rows, so the top of the 32-bit range is where a wrong stride
+    or a wrap would show."""
+    M, N, K = 32768, 72, 32760
+    assert M * K * 2 < 2 ** 31
+    print(f"[gpu] largest A {M}x{K}, N={N}, config {cid}", flush=True)
+    a, b = W.pattern_inputs(M, N, K, device=DEV)
+    c = gsr.gemm_scale_relu_ex(a, b, 0.5, cid)
+    torch.cuda.synchronize()
+    ms, ns = W.sample_points(M, N, 2048, seed=2, extra_rows=[M - 1])
+    ms = np.concatenate([ms, np.arange(M, dtype=np.int64)[::61]])
+    ns = np.concatenate([ns, np.arange(0, M, 61) % N])
+    ref, _ = orc.gemm_scale_relu_points(W.fp16_bits(a.cpu()), W.fp16_bits(b.cpu()), 0.5, ms, ns)
+    got = W.fp16_bits(c.cpu())
+    PT.assert_bitwise(f"largest cfg{cid}", got[ms, ns], ref)
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
 def test_concurrent_host_threads(gsr, tmp_path):
     """Eight host threads, each on its own stream, call the library with
     different shapes, configurations and epilogues while a ninth thread keeps
