@@ -22,6 +22,7 @@
 #include "gsr_interleave_h.hpp"
 #include "gsr_interleave_q.hpp"
 #include "gsr_interleave16.hpp"
+#include "gsr_interleave16h.hpp"
 
 namespace {
 
@@ -62,6 +63,12 @@ hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 hipError_t launch_ilv16(const Problem& p, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ilv16h(const Problem& p, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv16h_kernel, dim3(grid), dim3(gsr::Ilv16HCfg::NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -181,6 +188,8 @@ const Entry kTable[] = {
     Entry{{24, 128, 128, 64, 2, 2, 1, 4, 1, gsr::IlvQCfg::LDS_BYTES}, launch_ilvq, launch_staged<128, 128, 64, 2, 2, false>},
     // config 15's tile and data flow on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave)
     Entry{{25, 256, 256, 64, 2, 2, 1, 4, 1, gsr::Ilv16Cfg::LDS_BYTES}, launch_ilv16, launch_staged<256, 256, 64, 2, 2, false>},
+    // config 23's tile and data flow on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave)
+    Entry{{26, 128, 256, 64, 2, 2, 1, 4, 1, gsr::Ilv16HCfg::LDS_BYTES}, launch_ilv16h, launch_staged<128, 256, 64, 2, 2, false>},
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -189,13 +198,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.75, 0.4 + 0.6 * fill) of a full one (a part-filled chip
+// full costs max(0.30, 0.55 + 0.45 * fill) of a full one (a part-filled chip
 // runs at a higher power-limited clock, but every tile still pays its fixed
 // cost).  The 256x256 tile has two kernels: config 15 (32x32x16 MFMAs, the
 // higher issue efficiency) and config 25 (16x16x32 MFMAs, the higher engine
 // clock on random data once the power limit binds); config 25 takes config
-// 15's place when the 256x256 grid has at least 160 workgroups.  The rates,
-// overheads, the partial-wave form and the 160 were fitted (least squares in
+// 15's place when the 256x256 grid has at least 160 workgroups, and config 26
+// (16x16x32) takes that of config 23 (the 128x256 tile) from 176 workgroups of
+// 128x256.  The rates, overheads, the partial-wave form and the thresholds
+// were fitted (least squares in
 // relative error for the rates, then the grid point whose choices come
 // closest to the fastest configuration) to the times of every configuration
 // on 60 shapes measured on one MI355X (M from 1 to 8192 against 11008x4096,
@@ -212,33 +223,37 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {15, 6.05, 10.45},  // 256x256, explicit interleave, 32x32x16 (grids below 160 tiles)
-    {23, 4.31, 6.93},  // 128x256, explicit interleave
-    {24, 3.27, 5.02},   // 128x128, explicit interleave
-    {5, 3.73, 8.68},   // 256x128
-    {6, 3.59, 8.51},   // 128x256
-    {7, 3.12, 6.07},    // 128x128
-    {10, 2.01, 5.07},   // 64x128
-    {8, 2.20, 4.91},    // 128x64
-    {25, 5.27, 4.27},   // 256x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
-    {21, 2.70, 3.49},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.81, 2.65},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.40, 4.06},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.58, 3.06},   // 32x64, K split, four waves       (K <= 256)
+    {15, 5.31, 15.42},  // 256x256, explicit interleave, 32x32x16 (grids below 160 tiles)
+    {23, 3.95, 10.30},   // 128x256, explicit interleave, 32x32x16 (grids below 176 tiles)
+    {24, 3.36, 7.39},   // 128x128, explicit interleave
+    {5, 3.79, 13.49},   // 256x128
+    {6, 3.60, 13.42},   // 128x256
+    {7, 3.23, 8.68},    // 128x128
+    {10, 2.06, 6.63},   // 64x128
+    {8, 2.29, 6.46},    // 128x64
+    {25, 5.55, 7.32},   // 256x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
+    {26, 4.47, 6.76},   // 128x256, explicit interleave, 16x16x32 (grids of 176 tiles or more)
+    {21, 2.81, 3.76},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.84, 2.81},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.48, 4.45},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.60, 3.27},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.75, kPartA = 0.40;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr double kPartMin = 0.30, kPartA = 0.55;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 constexpr int64_t kFullChipTiles = 160;           // config 25 instead of config 15 from this many 256x256 tiles
+constexpr int64_t kFullChipTilesH = 176;          // config 26 instead of config 23 from this many 128x256 tiles
 
 int select(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
     const bool full_chip = cdiv(M, 256) * cdiv(N, 256) >= kFullChipTiles;
+    const bool full_chip_h = cdiv(M, 128) * cdiv(N, 256) >= kFullChipTilesH;
     int best = full_chip ? 25 : 15;
     double best_t = 1e300;
     for (const Candidate& c : kCandidates) {
         const bool copy_wave = c.id == 21 || c.id == 22, four_wave = c.id == 16 || c.id == 18;
         if ((copy_wave && K <= 256) || (four_wave && K > 256)) continue;
         if ((c.id == 15 && full_chip) || (c.id == 25 && !full_chip)) continue;
+        if ((c.id == 23 && full_chip_h) || (c.id == 26 && !full_chip_h)) continue;
         const gsr_config& g = kTable[c.id].cfg;
         const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
         const double full = std::floor(wgs / cus), fill = (wgs - full * cus) / cus;

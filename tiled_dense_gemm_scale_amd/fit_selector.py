@@ -6,14 +6,16 @@ The selector in csrc/gsr_api.hip prices a candidate tile bm x bn as
 
 with wgs = ceil(M / bm) * ceil(N / bn) workgroups on 256 CUs and
 waves(wgs) = full waves + (a part-filled last wave: max(pmin, a + (1 - a) * fill)).
-The 256x256 tile has two kernels: config 15 (32x32x16 MFMAs, the higher issue
-efficiency) and config 25 (16x16x32 MFMAs, the higher engine clock once enough
-CUs run for the power limit to bind); config 25 stands in for config 15 when
-the 256x256 grid has at least `full` workgroups.  This module fits `rate`
-(TFLOP/s per CU) and `tile_us` per configuration by least squares in relative
-error on the shapes where it is a candidate, for each (a, pmin, full) on a
-grid, and keeps the triple whose choices come closest to the fastest measured
-configuration (mean log ratio).  Input: the CSV written from a `tune.py --top 0` report
+The 256x256 and 128x256 tiles have two kernels each: one on 32x32x16 MFMAs
+(configs 15 and 23, the higher issue efficiency) and one on 16x16x32 MFMAs
+(configs 25 and 26, the higher engine clock once enough CUs run for the power
+limit to bind); config 25 stands in for config 15 when the 256x256 grid has
+at least full[0] workgroups, config 26 for config 23 when the 128x256 grid has
+at least full[1].  This module fits `rate` (TFLOP/s per CU) and `tile_us` per
+configuration by least squares in relative error on the shapes where it is a
+candidate, and picks (a, pmin, full) on grids whose choices come closest to
+the fastest measured configuration (mean log ratio): first (full[0], a, pmin)
+with config 26 left out, then full[1], then (a, pmin) again.  Input: the CSV written from a `tune.py --top 0` report
 (tuning/mi355x_config_times.csv) or such a JSON report itself.
 
     python -m tiled_dense_gemm_scale_amd.fit_selector tuning/mi355x_config_times.csv
@@ -39,13 +41,19 @@ Shape = Tuple[int, int, int]
 BASE = [15, 23, 24, 5, 6, 7, 10, 8]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
-FULL_CHIP = 25  # stands in for config 15 on grids of at least `full` 256x256 tiles
-ALL = BASE + [FULL_CHIP] + COPY_WAVE + FOUR_WAVE
+# (config, its 16x16x32 stand-in, the tile whose grid size decides)
+FULL_CHIP = [(15, 25, (256, 256)), (23, 26, (128, 256))]
+ALL = BASE + [f for _, f, _ in FULL_CHIP] + COPY_WAVE + FOUR_WAVE
 FULL_GRID = (64, 96, 128, 160, 192, 224, 256, 320)
+FULL_H_GRID = (128, 160, 176, 192, 208, 224, 256, 320)
+NEVER = 1 << 30
 
 
-def candidates(M: int, N: int, K: int, full: int) -> List[int]:
-    base = BASE if workgroups((256, 256), M, N) < full else [FULL_CHIP] + BASE[1:]
+def candidates(M: int, N: int, K: int, full) -> List[int]:
+    base = list(BASE)
+    for (cid, stand_in, tile), f in zip(FULL_CHIP, full):
+        if workgroups(tile, M, N) >= f:
+            base[base.index(cid)] = stand_in
     return base + (COPY_WAVE if K > 256 else FOUR_WAVE)
 
 
@@ -81,17 +89,20 @@ def workgroups(tile: Tuple[int, int], M: int, N: int) -> int:
     return -(-M // tile[0]) * -(-N // tile[1])
 
 
-def fit_params(times, tiles, a: float, pmin: float, full: int) -> Dict[int, Tuple[float, float]]:
+PAIRED = {c for c, _, _ in FULL_CHIP} | {f for _, f, _ in FULL_CHIP}
+
+
+def fit_params(times, tiles, a: float, pmin: float, full) -> Dict[int, Tuple[float, float]]:
     """(rate, tile_us) per candidate: least squares of t ~ w * (flops/rate + e),
-    rows scaled by 1/t (relative error); configs 15 and 25 on the shapes where
-    the full-chip rule makes them candidates."""
+    rows scaled by 1/t (relative error); the paired configurations on the
+    shapes where the full-chip rules make them candidates."""
     out = {}
     for cid in ALL:
         X, y = [], []
         for (M, N, K), t in times.items():
             if cid not in t:
                 continue
-            if cid in (15, FULL_CHIP) and cid not in candidates(M, N, K, full):
+            if cid in PAIRED and cid not in candidates(M, N, K, full):
                 continue
             w = waves(workgroups(tiles[cid], M, N), a, pmin)
             X.append([w * 2.0 * tiles[cid][0] * tiles[cid][1] * K / 1e6, w])
@@ -104,7 +115,7 @@ def fit_params(times, tiles, a: float, pmin: float, full: int) -> Dict[int, Tupl
     return out
 
 
-def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, full: int, have=None) -> int:
+def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, full, have=None) -> int:
     best, best_t = None, math.inf
     for cid in candidates(M, N, K, full):
         if cid not in params or (have is not None and cid not in have):
@@ -127,20 +138,30 @@ def regret(times, tiles, params, a, pmin, full) -> Tuple[float, float]:
     return math.exp(sum(logs) / len(logs)), worst
 
 
-def fit(times, tiles, a_grid=None, p_grid=None, full_grid=None):
-    """(mean, worst, a, pmin, full, params) of the best grid point."""
+def _search(times, tiles, a_grid, p_grid, fulls):
+    best = None
+    for full in fulls:
+        for a in a_grid:
+            for p in p_grid:
+                params = fit_params(times, tiles, float(a), float(p), full)
+                mean, worst = regret(times, tiles, params, float(a), float(p), full)
+                if best is None or mean < best[0] - 1e-12:
+                    best = (mean, worst, float(a), float(p), full, params)
+    return best
+
+
+def fit(times, tiles, a_grid=None, p_grid=None, full_grid=None, full_h_grid=None):
+    """(mean, worst, a, pmin, (full[0], full[1]), params) of the best point,
+    by coordinate search: (full[0], a, pmin) without config 26, then full[1],
+    then (a, pmin) again."""
     a_grid = np.arange(0.0, 0.75, 0.05) if a_grid is None else a_grid
     p_grid = np.arange(0.30, 0.90, 0.05) if p_grid is None else p_grid
     full_grid = FULL_GRID if full_grid is None else full_grid
-    best = None
-    for full in full_grid:
-        for a in a_grid:
-            for p in p_grid:
-                params = fit_params(times, tiles, float(a), float(p), int(full))
-                mean, worst = regret(times, tiles, params, float(a), float(p), int(full))
-                if best is None or mean < best[0] - 1e-12:
-                    best = (mean, worst, float(a), float(p), int(full), params)
-    return best
+    full_h_grid = FULL_H_GRID if full_h_grid is None else full_h_grid
+    best = _search(times, tiles, a_grid, p_grid, [(int(f), NEVER) for f in full_grid])
+    f0, a, p = best[4][0], best[2], best[3]
+    best = _search(times, tiles, [a], [p], [(f0, int(f)) for f in full_h_grid])
+    return _search(times, tiles, a_grid, p_grid, [best[4]])
 
 
 def main(argv=None) -> int:
@@ -151,7 +172,7 @@ def main(argv=None) -> int:
     times, tiles = load(args.times)
     mean, worst, a, p, full, params = fit(times, tiles)
     print(f"# {len(times)} shapes; waves: part-filled last wave costs max({p:.2f}, {a:.2f} + {1 - a:.2f} * fill);"
-          f" config {FULL_CHIP} for config 15 from {full} 256x256 tiles")
+          + "".join(f" config {f} for config {c} from {n} {t[0]}x{t[1]} tiles;" for (c, f, t), n in zip(FULL_CHIP, full)))
     for cid in ALL:
         if cid in params:
             bm, bn = tiles[cid]
