@@ -214,7 +214,7 @@ def test_unaligned_pointers(gsr, orc, offset):
     PT.assert_parity(f"unaligned+{offset}", bits(cd.cpu()), ref)
 
 
-@pytest.mark.parametrize("cid", [-1, 0, 5, 15, 21, 23, 24, 25])
+@pytest.mark.parametrize("cid", [-1, 0, 5, 15, 21, 23, 24, 25, 26])
 def test_guard_bands_and_full_coverage(gsr, orc, cid):
     """C sits inside a larger buffer filled with a sentinel: the bands before
     and after stay untouched and every element of C is written."""

@@ -47,12 +47,12 @@ def test_largest_operand_under_2gib(gsr, orc, K):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cid", [15, 25])
-def test_largest_operand_under_2gib_256_tiles(gsr, orc, cid):
-    """The same A just under 2^31 bytes through each 256x256 kernel, forced:
-    their per-lane copy offsets are formed from base registers plus strides
-    of 32 and 64 rows, so the top of the 32-bit range is where a wrong stride
-    or a wrap would show."""
+@pytest.mark.parametrize("cid", [15, 23, 25, 26])
+def test_largest_operand_under_2gib_interleaved(gsr, orc, cid):
+    """The same A just under 2^31 bytes through each interleaved 256x256 and
+    128x256 kernel, forced: their per-lane copy offsets are formed from base
+    registers plus strides of 32 and 64 rows, so the top of the 32-bit range
+    is where a wrong stride or a wrap would show."""
     M, N, K = 32768, 72, 32760
     assert M * K * 2 < 2 ** 31
     print(f"[gpu] largest A {M}x{K}, N={N}, config {cid}", flush=True)
