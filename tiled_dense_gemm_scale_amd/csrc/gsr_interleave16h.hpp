@@ -51,75 +51,6 @@ struct Ilv16HCfg {
     static_assert(A_PER == 4 && FM == 4 && FN == 8 && SLOTS == 32, "the slot plan below");
 };
 
-// The epilogue of the 16x16 layout for a WTM x WTN wave sub-tile (the same
-// steps as ilv16_epilogue): lane l holds, for block (a, b), rows
-// m = 16b + l % 16 and columns n = 16a + 4(l / 16) + 0..3 of the sub-tile;
-// each wave stages its fp16 sub-tile in its own LDS rows (16-byte chunk c of
-// row r at physical chunk c ^ (r % 16)) and stores 256-byte row segments.
-template <class T>
-__device__ __forceinline__ void ilv16_epilogue_t(const Problem& p, const f32x4 (&acc)[T::FN][T::FM], uint8_t* smem,
-                                                 int m0, int n0, int wm, int wn, int wave)
-{
-    constexpr int FM = T::FM, FN = T::FN;
-    const uint32_t lane = (uint32_t)(threadIdx.x & 63);
-    const uint32_t lrow = lane & 15u, lq = lane >> 4;
-    const uint32_t N = (uint32_t)p.N;
-    constexpr uint32_t CPR = T::WTN / 8, RB = T::WTN * 2;  // 16 chunks, 256 bytes per staging row
-    static_assert(T::WTN == 128 && T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "staging rows of 16 chunks fit");
-    const bool plain = plain_epilogue(p);
-    f32x4 bvs[FN];
-    {
-        const __amdgpu_buffer_rsrc_t rbias = bias_rsrc(p);
-        const bool load = !plain && p.bias != nullptr;
-#pragma unroll
-        for (int a = 0; a < FN; ++a)
-            bvs[a] = load ? bias4(rbias, n0 + wn * T::WTN + a * 16 + 4 * (int)lq) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    lds_barrier();  // every wave is past its last operand read
-    const float alpha = p.alpha;
-    uint8_t* const ep = smem + wave * (T::WTM * T::WTN * 2);
-    auto stage4 = [&](int a, int b, half4 h) {
-        const uint32_t r = (uint32_t)b * 16u + lrow;
-        const uint32_t c = ((uint32_t)(2 * a) + (lq >> 1)) ^ (r & (CPR - 1u));
-        *(u32x2*)(ep + r * RB + c * 16u + (lq & 1u) * 8u) = __builtin_bit_cast(u32x2, h);
-    };
-    if (plain) {
-#pragma unroll
-        for (int a = 0; a < FN; ++a)
-#pragma unroll
-            for (int b = 0; b < FM; ++b) {
-                half4 h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = acc[a][b][i] * alpha;
-                    h[i] = (_Float16)(v > 0.0f ? v : 0.0f);
-                }
-                stage4(a, b, h);
-            }
-    } else {
-        with_activation(p.act, [&](auto act_tag) {
-            constexpr int ACT = decltype(act_tag)::value;
-#pragma unroll
-            for (int a = 0; a < FN; ++a)
-#pragma unroll
-                for (int b = 0; b < FM; ++b) stage4(a, b, epilogue4<ACT>(acc[a][b], alpha, bvs[a]));
-        });
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * N * 2u);
-    constexpr uint32_t RPI = 64u / CPR;  // rows per store instruction
-    const uint32_t sc = lane & (CPR - 1u);
-    const int n = n0 + wn * T::WTN + 8 * (int)sc;
-#pragma unroll
-    for (int j = 0; j < (int)(T::WTM / RPI); ++j) {
-        const uint32_t r = RPI * (uint32_t)j + lane / CPR;
-        const u32x4 v = *(const u32x4*)(ep + r * RB + ((sc ^ (r & (CPR - 1u))) << 4));
-        const int m = m0 + wm * T::WTM + (int)r;
-        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
-    }
-}
-
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_scale_relu_ilv16h_kernel(Problem p)
 {
