@@ -1,7 +1,8 @@
 """GPU robustness: the largest problems the 32-bit byte offsets allow (on the
 128-bit and the element-wise path), concurrent calls from several host
-threads on their own streams while the tuning table changes, and graph
-capture of the epilogue variants replayed against eager results."""
+threads on their own streams while the tuning table changes, graph
+capture of the epilogue variants replayed against eager results, and a good
+launch while an unrelated HIP error is pending on the thread."""
 import threading
 
 import numpy as np
@@ -163,3 +164,36 @@ def test_graph_capture_of_variants(gsr, act, with_bias):
             assert torch.equal(o.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
         gsr.gemm_scale_relu(ad, bd, 0.5)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_pending_unrelated_hip_error_is_not_taken_for_a_launch_error(gsr, orc):
+    """A HIP error that an earlier call left pending on the thread (here a
+    failed hipSetDevice, a host-side check that touches no device) must not
+    turn a good launch into GSR_ERROR_LAUNCH, on the tile path nor on the
+    K = 0 fill; the caller's pending error is left for the caller."""
+    import ctypes
+
+    from tiled_dense_gemm_scale_amd import _native as nat
+
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and the library already share
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    M, N, K = 200, 136, 72
+    a, b = W.integer_inputs(M, N, K, seed=3)
+    ref, _ = orc.gemm_scale_relu(W.fp16_bits(a), W.fp16_bits(b), 0.5)
+    ad, bd = a.to(DEV), b.to(DEV)
+    c = torch.full((M, N), 7.0, dtype=torch.float16, device=DEV)
+    c0 = torch.full((M, N), 7.0, dtype=torch.float16, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    print("[gpu] launch with an unrelated HIP error pending", flush=True)
+    bad = hip.hipSetDevice(1 << 20)
+    try:
+        assert bad != 0 and hip.hipPeekAtLastError() == bad
+        st = nat.gemm_scale_relu(M, N, K, ad.data_ptr(), bd.data_ptr(), c.data_ptr(), 0.5, stream)
+        st0 = nat.gemm_scale_relu(M, N, 0, ad.data_ptr(), bd.data_ptr(), c0.data_ptr(), 0.5, stream)
+    finally:
+        hip.hipGetLastError()  # clear it before torch launches anything
+    assert (st, st0) == (0, 0), (st, st0)
+    torch.cuda.synchronize()
+    PT.assert_bitwise("pending-error launch", W.fp16_bits(c.cpu()), ref)
+    assert not torch.any(c0.view(torch.int16) != 0)

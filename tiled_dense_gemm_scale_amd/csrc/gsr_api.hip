@@ -30,78 +30,83 @@ using gsr::Problem;
 
 typedef hipError_t (*launch_fn)(const Problem&, int grid, hipStream_t);
 
+template <typename T>
+struct as_is {
+    using type = T;
+};
+
+// Enqueues `kernel` and returns the status of this launch alone.  The status
+// comes from hipLaunchKernel's return value, not from hipGetLastError: an
+// error that an earlier, unrelated HIP call left pending on the calling
+// thread is neither reported as this launch's nor cleared.
+template <typename... P>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, typename as_is<P>::type... args)
+{
+    void* argv[] = {(void*)&args...};
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, 0, s);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, bool VEC>
 hipError_t launch_staged(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gsr::gemm_scale_relu_kernel<BM, BN, BK, WM, WN, VEC>), dim3(grid),
-                       dim3(gsr::kWave * WM * WN), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel((gsr::gemm_scale_relu_kernel<BM, BN, BK, WM, WN, VEC>), dim3(grid),
+                         dim3(gsr::kWave * WM * WN), s, p);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int S>
 hipError_t launch_pipe(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gsr::gemm_scale_relu_pipe_kernel<BM, BN, BK, WM, WN, S>), dim3(grid),
-                       dim3(gsr::kWave * WM * WN), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel((gsr::gemm_scale_relu_pipe_kernel<BM, BN, BK, WM, WN, S>), dim3(grid),
+                         dim3(gsr::kWave * WM * WN), s, p);
 }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gsr::gemm_scale_relu_bt_kernel<BM, BN, WM, WN>), dim3(grid), dim3(gsr::kWave * WM * WN), 0, s,
-                       p);
-    return hipGetLastError();
+    return launch_kernel((gsr::gemm_scale_relu_bt_kernel<BM, BN, WM, WN>), dim3(grid),
+                         dim3(gsr::kWave * WM * WN), s, p);
 }
 
 hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), s, p);
 }
 
 hipError_t launch_ilv16(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), s, p);
 }
 
 hipError_t launch_ilv16h(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilv16h_kernel, dim3(grid), dim3(gsr::Ilv16HCfg::NT), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_ilv16h_kernel, dim3(grid), dim3(gsr::Ilv16HCfg::NT), s, p);
 }
 
 hipError_t launch_ilvh(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilvh_kernel, dim3(grid), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_ilvh_kernel, dim3(grid), dim3(256), s, p);
 }
 
 hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_ilvq_kernel, dim3(grid), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_ilvq_kernel, dim3(grid), dim3(256), s, p);
 }
 
 hipError_t launch_dual(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(gsr::gemm_scale_relu_dual_kernel, dim3(grid), dim3(gsr::DualCfg::NT), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gsr::gemm_scale_relu_dual_kernel, dim3(grid), dim3(gsr::DualCfg::NT), s, p);
 }
 
 template <int BM, int BN, int S>
 hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gsr::gemm_scale_relu_ksplit_kernel<BM, BN, S>), dim3(grid), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel((gsr::gemm_scale_relu_ksplit_kernel<BM, BN, S>), dim3(grid), dim3(256), s, p);
 }
 
 template <int BM, int BN, int S, int D>
 hipError_t launch_kspec(const Problem& p, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((gsr::gemm_scale_relu_kspec_kernel<BM, BN, S, D>), dim3(grid), dim3(512), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel((gsr::gemm_scale_relu_kspec_kernel<BM, BN, S, D>), dim3(grid), dim3(512), s, p);
 }
 
 struct Entry {
@@ -432,9 +437,9 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     if (K == 0) {
         const uint32_t count = (uint32_t)(M * N);
         const int grid = (int)std::min<int64_t>(cdiv(count, 256), 4096);
-        hipLaunchKernelGGL(gsr::fill_epilogue_kernel, dim3(grid), dim3(256), 0, s, (uint16_t*)C, (uint32_t)M,
-                           (uint32_t)N, (const uint16_t*)bias, alpha, (int)activation);
-        return hipGetLastError() == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
+        const hipError_t err = launch_kernel(gsr::fill_epilogue_kernel, dim3(grid), dim3(256), s, (uint16_t*)C,
+                                             (uint32_t)M, (uint32_t)N, (const uint16_t*)bias, alpha, (int)activation);
+        return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
     }
 
     const Launch l = (forced == -2) ? given : resolve(M, N, K, forced);
