@@ -191,3 +191,32 @@ def test_launch_entry_point_checks(native):
     for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (7, 0, 1), (7, 5000, 1), (7, 4, 2)):
         st = native.gemm_scale_bias_act_cfg(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 0, 0, cid, gm, xcd)
         assert st == 6, (cid, gm, xcd, st)
+
+
+class _DeviceTensorStandIn:
+    """Carries only the attributes the binding's operand checks read, so the
+    checks run without a GPU; no data is ever touched."""
+
+    def __init__(self, shape, index):
+        import torch
+
+        self.shape, self.dtype, self.is_cuda = tuple(shape), torch.float16, True
+        self.device = torch.device("cuda", index)
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return True
+
+
+def test_binding_rejects_operands_on_different_devices():
+    import tiled_dense_gemm_scale_amd as gsr
+
+    T = _DeviceTensorStandIn
+    with pytest.raises(ValueError, match="one device"):
+        gsr.gemm_scale_relu(T((4, 8), 0), T((8, 4), 1), 0.5)
+    with pytest.raises(ValueError, match="A's device"):
+        gsr.gemm_scale_relu(T((4, 8), 0), T((8, 4), 0), 0.5, c=T((4, 4), 1))
+    with pytest.raises(ValueError, match="A's device"):
+        gsr.gemm_scale_bias_act(T((4, 8), 0), T((8, 4), 0), T((4,), 1), c=T((4, 4), 0))

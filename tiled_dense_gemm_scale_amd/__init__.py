@@ -41,6 +41,8 @@ def _check_operands(a: torch.Tensor, b: torch.Tensor, c: Optional[torch.Tensor])
         raise ValueError(f"shape mismatch: A {tuple(a.shape)} @ B {tuple(b.shape)}")
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("A and B must be device tensors")
+    if b.device != a.device:
+        raise ValueError(f"A and B must be on one device, got {a.device} and {b.device}")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("A and B must be row-major contiguous")
     M, K = a.shape
@@ -49,6 +51,8 @@ def _check_operands(a: torch.Tensor, b: torch.Tensor, c: Optional[torch.Tensor])
         c = torch.empty((M, N), dtype=torch.float16, device=a.device)
     elif c.dtype != torch.float16 or tuple(c.shape) != (M, N) or not c.is_contiguous() or not c.is_cuda:
         raise ValueError("C must be a contiguous (M,N) float16 device tensor")
+    elif c.device != a.device:
+        raise ValueError(f"C must be on A's device {a.device}, got {c.device}")
     return int(M), int(N), int(K), c
 
 
@@ -94,8 +98,9 @@ def gemm_scale_bias_act(a: torch.Tensor, b: torch.Tensor, bias: Optional[torch.T
         raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
     bptr = 0
     if bias is not None:
-        if bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous():
-            raise ValueError(f"bias must be a contiguous ({N},) float16 device tensor")
+        if (bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous()
+                or bias.device != a.device):
+            raise ValueError(f"bias must be a contiguous ({N},) float16 tensor on A's device")
         bptr = bias.data_ptr()
     with torch.cuda.device(a.device):
         s = _stream_handle(a.device, stream)
@@ -115,8 +120,9 @@ def gemm_launch(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id: int, 
         raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
     bptr = 0
     if bias is not None:
-        if bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous():
-            raise ValueError(f"bias must be a contiguous ({N},) float16 device tensor")
+        if (bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous()
+                or bias.device != a.device):
+            raise ValueError(f"bias must be a contiguous ({N},) float16 tensor on A's device")
         bptr = bias.data_ptr()
     with torch.cuda.device(a.device):
         s = _stream_handle(a.device, stream)
