@@ -172,10 +172,16 @@ def test_pending_unrelated_hip_error_is_not_taken_for_a_launch_error(gsr, orc):
     turn a good launch into GSR_ERROR_LAUNCH, on the tile path nor on the
     K = 0 fill; the caller's pending error is left for the caller."""
     import ctypes
+    import os
 
     from tiled_dense_gemm_scale_amd import _native as nat
 
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and the library already share
+    # the HIP runtime torch and the library already share: reopen that very
+    # file (dlopen returns the loaded copy), never load a second runtime
+    nat.lib()
+    loaded = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln.split()[-1]})
+    assert len(loaded) == 1, loaded
+    hip = ctypes.CDLL(loaded[0], mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
     hip.hipSetDevice.argtypes = [ctypes.c_int]
     M, N, K = 200, 136, 72
     a, b = W.integer_inputs(M, N, K, seed=3)
