@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2516.6   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-DEFAULT_WORKLOAD = "square_1024"
+DEFAULT_WORKLOAD = "square_16384"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -97,6 +97,76 @@ def device_info(index: int) -> dict:
         if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, index) == 0:
             info[key] = v.value
     return info
+
+
+class ClockSampler:
+    """The engine (graphics) clock the GPU reports while the timed calls run,
+    read through amdsmi in a background thread every `period_s` seconds.  The
+    part is power-limited under dense fp16 MFMA work, so this clock, not the
+    maximum the runtime reports, is what the achieved rate follows.  Sampling
+    only reads the driver's counters; any failure (no amdsmi, no permission,
+    the device not found) leaves the result None."""
+
+    def __init__(self, props, period_s: float = 0.004):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        self._amdsmi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            want = (int(props.pci_domain_id), int(props.pci_bus_id), int(props.pci_device_id))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._handle = h
+                    break
+            if self._handle is None:
+                self.error = f"no amdsmi device at {want}"
+        except Exception as e:  # noqa: BLE001 - a missing clock reading is not an error of the benchmark
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.SYS)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        """Median, min and max of the samples in MHz, or None."""
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "source": "amdsmi graphics clock, sampled every ~4 ms while the timed graph and its repeats ran"}
 
 
 def time_graph(graph, stream, steps: int, repeats: int):
@@ -284,7 +354,9 @@ def main(argv=None) -> int:
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler(props)
     torch.cuda.synchronize()  # single rank: the barrier is this synchronise
+    clock.start()
     start.record(stream)
     if graph is not None:
         with torch.cuda.stream(stream):
@@ -313,6 +385,12 @@ def main(argv=None) -> int:
         context["repeat_ms_per_step"] = {"median": round(reps[len(reps) // 2], 6), "min": round(reps[0], 6),
                                          "max": round(reps[-1], 6), "n": len(reps)}
         log(f"[bench] repeats: {context['repeat_ms_per_step']}")
+    observed = clock.stop()
+    context["engine_clock_observed"] = observed
+    if observed is None:
+        log(f"[bench] engine clock not sampled ({clock.error})")
+    else:
+        log(f"[bench] engine clock while timed: {observed}")
     if graph is not None and not args.no_context:
         a0 = torch.empty((1, 0), dtype=torch.float16, device=dev)
         b0 = torch.empty((0, 8), dtype=torch.float16, device=dev)

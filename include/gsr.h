@@ -60,10 +60,13 @@ enum gsr_activation {
 /* One compiled tile configuration.  A workgroup of waves_m*waves_n wave64s
  * owns a block_m x block_n tile of C and walks K in steps of block_k through
  * `stages` LDS buffers; each wave owns a (block_m/waves_m) x (block_n/waves_n)
- * sub-tile built from 32x32x16 fp16 MFMAs (config 25, the same 256x256 tile
- * as config 15: 16x16x32 fp16 MFMAs).  group_m is the number of tile rows
- * in one group of the grouped launch order, xcd_remap says whether workgroup
- * ids are regrouped so that neighbouring tiles run on the same XCD. */
+ * sub-tile.  Configurations 25 and 26 build that sub-tile from 16x16x32 fp16
+ * MFMAs, all others from 32x32x16 fp16 MFMAs.  (The K-split kinds, block_k
+ * 128 with waves 1 x 1, give every wave the whole tile and a share of each
+ * K-step instead.)  group_m is the number of tile rows in one group of the
+ * grouped launch order, xcd_remap says whether workgroup ids are regrouped so
+ * that neighbouring tiles run on the same XCD.  Ids are stable across library
+ * versions and not contiguous: gsr_config_ids lists the compiled ones. */
 typedef struct gsr_config {
     int32_t id;
     int32_t block_m, block_n, block_k;
@@ -77,15 +80,16 @@ typedef struct gsr_config {
 /* The fused operation (the tutorial's kernel call: A, B, C, scale).
  * M, N, K >= 0.  M == 0 or N == 0: success, nothing enqueued.  K == 0: every
  * output is the empty sum, C is filled with +0.  Any pointer alignment of at
- * least 2 bytes is accepted; 16-byte aligned A and B, 8-byte aligned C and
- * K, N multiples of 8 take the 128-bit vector path, anything else an
- * element-wise path of the same kernel.  Returns a gsr_status. */
+ * least 2 bytes is accepted; 16-byte aligned A, B and C with K and N
+ * multiples of 8 take the 128-bit vector path, anything else an element-wise
+ * path (a register-staged kernel of the same tile, or of a 64x64 tile for the
+ * K-split kinds).  Returns a gsr_status. */
 int gemm_scale_relu(int64_t M, int64_t N, int64_t K,
                     const void* A, const void* B, void* C,
                     float alpha, void* stream);
 
-/* As gemm_scale_relu with a forced tile configuration (config_id from
- * gsr_get_config; -1 = the selector's choice).  For sweeps and tests. */
+/* As gemm_scale_relu with a forced tile configuration (an id from
+ * gsr_config_ids; -1 = the selector's choice).  For sweeps and tests. */
 int gemm_scale_relu_ex(int64_t M, int64_t N, int64_t K,
                        const void* A, const void* B, void* C,
                        float alpha, void* stream, int32_t config_id);
@@ -149,8 +153,12 @@ int gsr_tuning_entries(void);
  * touches no device.  Returns GSR_SUCCESS or GSR_ERROR_INVALID_VALUE. */
 int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out);
 
-/* Number of compiled tile configurations, and the description of one. */
+/* Number of compiled tile configurations; their ids (written to ids[0..],
+ * at most `capacity` of them; returns the number of compiled configurations,
+ * or -1 for capacity < 0 or a null ids with capacity > 0); the description of
+ * one (GSR_ERROR_INVALID_CONFIG for an id that is not compiled).  Host only. */
 int gsr_num_configs(void);
+int gsr_config_ids(int32_t* ids, int32_t capacity);
 int gsr_get_config(int32_t config_id, gsr_config* out);
 
 /* A static, human-readable name for a status code. */

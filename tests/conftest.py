@@ -25,9 +25,10 @@ def orc():
 
 @pytest.fixture(scope="session")
 def native():
-    """The C-ABI library (built in-tree with hipcc if it is not there yet)."""
+    """The C-ABI library, built in-tree with hipcc first if it is missing or
+    older than its sources (the digest the build recorded beside it)."""
     from tiled_dense_gemm_scale_amd import _native, build
 
-    if not os.path.exists(_native.LIBRARY):
-        build.build()
+    if build.is_stale(_native.LIBRARY):
+        build.build(_native.LIBRARY)
     return _native

@@ -5,7 +5,9 @@ Tolerance (the tutorial's own check, PKUHPC scow-tutorial "Tutorial14",
 section 2 listing: assert_close with rtol = atol = 1e-2): every checked
 output must satisfy |gpu - ref| <= 1e-2 + 1e-2 * |ref|, with both the GPU
 output and the oracle's fp16 output decoded exactly; a NaN or Inf where the
-oracle is finite fails; +0 and -0 compare equal.
+oracle is finite fails; where the oracle itself is not finite (an fp16
+overflow to +-inf) only the identical bit pattern passes, since no finite
+bound can be formed there; +0 and -0 compare equal.
 """
 from __future__ import annotations
 
@@ -63,24 +65,31 @@ class Report:
 
 
 def compare(name: str, gpu_bits: np.ndarray, ref_bits: np.ndarray, coords=None) -> Report:
-    g = f16(gpu_bits).ravel()
-    r = f16(ref_bits).ravel()
+    gb = np.asarray(gpu_bits, dtype=np.uint16).ravel()
+    rb = np.asarray(ref_bits, dtype=np.uint16).ravel()
+    g = f16(gb)
+    r = f16(rb)
     if g.shape != r.shape:
         raise AssertionError(f"{name}: {g.shape} values vs {r.shape} expected")
     if g.size == 0:
         return Report(name, 0, 0.0, 0.0, 0, None, 0.0)
-    nonfinite = ~np.isfinite(g) & np.isfinite(r)
-    err = np.abs(g - r)
-    err[nonfinite] = np.inf
-    bound = ATOL + RTOL * np.abs(r)
+    fin = np.isfinite(r)
+    err = np.zeros_like(r)
+    bound = np.ones_like(r)
+    err[fin] = np.abs(g[fin] - r[fin])          # NaN where the GPU gave NaN
+    err[fin & ~np.isfinite(g)] = np.inf          # Inf or NaN where the oracle is finite
+    bound[fin] = ATOL + RTOL * np.abs(r[fin])
+    err[~fin] = np.where(gb[~fin] == rb[~fin], 0.0, np.inf)  # not finite: same bits or fail
     ratio = err / bound
-    viol = int(np.count_nonzero(ratio > 1.0) + np.count_nonzero(np.isnan(err) & np.isfinite(r)))
-    i = int(np.nanargmax(ratio))
+    viol = int(np.count_nonzero(~(ratio <= 1.0)))  # NaN counts as a violation
+    i = int(np.argmax(np.where(np.isnan(ratio), np.inf, ratio)))
     where = (tuple(np.unravel_index(i, np.asarray(ref_bits).shape)) if coords is None
              else (int(coords[0][i]), int(coords[1][i])))
-    denom = float(np.sqrt(np.sum(r * r)))
-    fro = float(np.sqrt(np.sum((g - r) ** 2)) / denom) if denom > 0 else float(np.sqrt(np.sum(g * g)))
-    return Report(name, g.size, float(np.nanmax(err)), float(np.nanmax(ratio)), viol, where, fro)
+    gf, rf = g[fin & np.isfinite(g)], r[fin & np.isfinite(g)]
+    denom = float(np.sqrt(np.sum(rf * rf)))
+    fro = float(np.sqrt(np.sum((gf - rf) ** 2)) / denom) if denom > 0 else float(np.sqrt(np.sum(gf * gf)))
+    return Report(name, g.size, float(np.max(np.where(np.isnan(err), np.inf, err))),
+                  float(np.max(np.where(np.isnan(ratio), np.inf, ratio))), viol, where, fro)
 
 
 def assert_parity(name: str, gpu_bits, ref_bits, coords=None) -> Report:

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "gemm_scale_bias_act_ex",
-              "gsr_select_config", "gsr_num_configs", "gsr_get_config", "gsr_status_string", "gsr_version"):
+              "gsr_select_config", "gsr_num_configs", "gsr_config_ids", "gsr_get_config", "gsr_status_string",
+              "gsr_version"):
         assert n in names
 
 
@@ -37,10 +38,16 @@ def test_config_struct_layout(native):
     assert ctypes.sizeof(native.GsrConfig) == 40
 
 
+# Ids of configurations dropped from the table; they are never reused.
+RETIRED_IDS = (0, 1, 2, 3, 4, 9, 11, 12, 13, 14, 19, 20)
+
+
 def test_config_table(native):
     n = native.num_configs()
-    assert n >= 4
-    for i in range(n):
+    ids = native.config_ids()
+    assert n >= 4 and len(ids) == n and ids == sorted(set(ids))
+    assert not set(ids) & set(RETIRED_IDS)
+    for i in ids:
         c = native.get_config(i)
         assert c["id"] == i
         assert c["block_k"] in (32, 64, 128)
@@ -51,10 +58,23 @@ def test_config_table(native):
         buffers = 2 if c["stages"] in (0, 1) else c["stages"]
         lds = buffers * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
         assert c["lds_bytes"] == lds <= 163840
-    with pytest.raises(native.GsrError):
-        native.get_config(n)
-    with pytest.raises(native.GsrError):
-        native.get_config(-1)
+    for bad in (-1, max(ids) + 1) + RETIRED_IDS:
+        with pytest.raises(native.GsrError):
+            native.get_config(bad)
+    # the id listing honours its capacity and rejects a bad one
+    buf = (ctypes.c_int32 * 2)(-7, -7)
+    assert native.lib().gsr_config_ids(buf, 1) == n and buf[0] == ids[0] and buf[1] == -7
+    assert native.lib().gsr_config_ids(None, 0) == n
+    assert native.lib().gsr_config_ids(None, 3) == -1
+    assert native.lib().gsr_config_ids(buf, -1) == -1
+
+
+def test_retired_ids_are_rejected_before_any_device_use(native):
+    """A forced launch of a retired or unknown id fails with
+    GSR_ERROR_INVALID_CONFIG from the host-side checks (no device needed)."""
+    for bad in RETIRED_IDS + (27, 1000):
+        st = native.gemm_scale_relu_ex(8, 8, 8, 0x1000, 0x2000, 0x3000, 1.0, 0, bad)
+        assert st == native.GSR_ERROR_INVALID_CONFIG, (bad, st)
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 256), (1024, 1024, 1024), (4096, 4096, 4096),
@@ -62,7 +82,7 @@ def test_config_table(native):
                                    (1, 1, 1), (0, 5, 5)])
 def test_selector(native, shape):
     c = native.select_config(*shape)
-    assert 0 <= c["id"] < native.num_configs()
+    assert c["id"] in native.config_ids()
     M, N, _ = shape
     if M * N >= 256 * 256 * 256:
         # large problems use a tile that still yields one workgroup per CU
@@ -167,6 +187,7 @@ def test_tuning_table_host_side(native, tmp_path):
         assert (c["id"], c["group_m"], c["xcd_remap"]) == (15, 8, 1)
         assert native.select_config(1024, 1024, 1025) == other  # not in the table
         for bad in ("1024 1024 1024 99 1 0\n",      # unknown config id
+                    "1024 1024 1024 9 1 0\n",       # a retired config id
                     "1024 1024 1024 7 0 0\n",       # group_m < 1
                     "1024 1024 1024 7 1 2\n",       # xcd_remap not 0/1
                     "1024 1024 7 1 0\n",            # too few fields

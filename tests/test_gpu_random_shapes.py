@@ -54,7 +54,7 @@ def test_random_shape_every_config_bitwise(gsr, orc, i):
     alpha = ALPHAS[i % len(ALPHAS)]
     a, b = W.integer_inputs(M, N, K, seed=100 + i)
     ref, _ = orc.gemm_scale_relu(W.fp16_bits(a), W.fp16_bits(b), alpha)
-    for cid in [-1] + list(range(gsr.num_configs())):
+    for cid in [-1] + gsr.config_ids():
         print(f"[gpu] random shape {M}x{N}x{K} alpha={alpha} config {cid}", flush=True)
         got = PT.run_gpu(a, b, alpha, config_id=cid)
         PT.assert_bitwise(f"{M}x{N}x{K} alpha={alpha} cfg{cid}", got, ref)

@@ -24,7 +24,7 @@ def gsr(native):
     g.clear_tuning()
 
 
-@pytest.mark.parametrize("cid", [15, 16, 7, 9, 18, 21, 22])
+@pytest.mark.parametrize("cid", [15, 16, 7, 18, 21, 22, 24, 25, 26])
 def test_launch_order_does_not_change_results(gsr, orc, cid):
     M, N, K = 700, 1100, 264
     a, b = W.normal_inputs(M, N, K, seed=cid)
@@ -46,7 +46,7 @@ def test_tuning_table_steers_the_plain_call(gsr, tmp_path):
     a, b = W.normal_inputs(M, N, K, seed=3)
     ad, bd = a.to(DEV), b.to(DEV)
     sel = gsr.select_config(M, N, K)["id"]
-    forced = 7 if sel != 7 else 9
+    forced = 7 if sel != 7 else 8
     want = gsr.gemm_scale_relu_ex(ad, bd, 0.5, forced).clone()
     p = tmp_path / "tuning.txt"
     p.write_text(f"{M} {N} {K} {forced} 2 0\n")

@@ -24,11 +24,12 @@ from typing import Optional
 import torch
 
 from . import _native
-from ._native import (GsrError, clear_tuning, get_config, load_tuning, num_configs, select_config, status_string,
-                      tuning_entries, version)
+from ._native import (GsrError, clear_tuning, config_ids, get_config, load_tuning, num_configs, select_config,
+                      status_string, tuning_entries, version)
 
 __all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "gemm_launch", "GsrError",
-           "select_config", "get_config", "num_configs", "status_string", "version", "configs", "ACTIVATIONS",
+           "select_config", "get_config", "num_configs", "config_ids", "status_string", "version", "configs",
+           "ACTIVATIONS",
            "load_tuning", "clear_tuning", "tuning_entries"]
 
 ACTIVATIONS = {"relu": _native.GSR_ACT_RELU, "gelu": _native.GSR_ACT_GELU, "none": _native.GSR_ACT_NONE}
@@ -133,5 +134,5 @@ def gemm_launch(a: torch.Tensor, b: torch.Tensor, alpha: float, config_id: int, 
 
 
 def configs() -> list:
-    """Every compiled tile configuration."""
-    return [get_config(i) for i in range(num_configs())]
+    """Every compiled tile configuration, by ascending id."""
+    return [get_config(i) for i in config_ids()]

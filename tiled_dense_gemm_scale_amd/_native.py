@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             L.gsr_select_config.restype = ctypes.c_int
             L.gsr_num_configs.argtypes = []
             L.gsr_num_configs.restype = ctypes.c_int
+            L.gsr_config_ids.argtypes = [ctypes.POINTER(i32), i32]
+            L.gsr_config_ids.restype = ctypes.c_int
             L.gsr_get_config.argtypes = [i32, ctypes.POINTER(GsrConfig)]
             L.gsr_get_config.restype = ctypes.c_int
             L.gsr_status_string.argtypes = [ctypes.c_int]
@@ -158,6 +160,17 @@ def select_config(M: int, N: int, K: int) -> dict:
 
 def num_configs() -> int:
     return int(lib().gsr_num_configs())
+
+
+def config_ids() -> list:
+    """The ids of the compiled tile configurations, ascending (ids are stable
+    across library versions and not contiguous)."""
+    n = int(lib().gsr_num_configs())
+    buf = (ctypes.c_int32 * max(n, 1))()
+    got = int(lib().gsr_config_ids(buf, n))
+    if got != n:
+        raise GsrError(GSR_ERROR_INVALID_VALUE, f"gsr_config_ids returned {got}, expected {n}")
+    return [int(buf[i]) for i in range(n)]
 
 
 def get_config(config_id: int) -> dict:

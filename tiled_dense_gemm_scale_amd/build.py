@@ -5,6 +5,7 @@ Usage: python -m tiled_dense_gemm_scale_amd.build [--verbose]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import os
 import shutil
 import subprocess
@@ -16,7 +17,37 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgsr.so")
 SOURCES = [os.path.join(CSRC, "gsr_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "gsr_kernels.hpp"), os.path.join(INCLUDE, "gsr.h")]
+# The digest of the sources a build used is written beside the library, so a
+# library older than its sources can be told apart from a current one.
+DIGEST_SUFFIX = ".sources"
+
+
+def depends() -> list:
+    """Every file the library is compiled from: the kernel and launch sources
+    and the public header."""
+    return sorted(os.path.join(CSRC, n) for n in os.listdir(CSRC)) + [os.path.join(INCLUDE, "gsr.h")]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for path in depends():
+        with open(path, "rb") as f:
+            h.update(os.path.relpath(path, ROOT).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def is_stale(output: str = LIBRARY) -> bool:
+    """True when the library is missing, or was built from other sources than
+    the current ones.  A library without a recorded digest (built elsewhere and
+    copied in) is taken as it is."""
+    if not os.path.exists(output):
+        return True
+    try:
+        with open(output + DIGEST_SUFFIX) as f:
+            return f.read().strip() != source_digest()
+    except FileNotFoundError:
+        return False
 
 
 def hipcc() -> str:
@@ -41,7 +72,10 @@ def build(output: str = LIBRARY, verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err:
         print(err)
+    digest = source_digest()
     os.replace(output + ".tmp", output)
+    with open(output + DIGEST_SUFFIX, "w") as f:
+        f.write(digest + "\n")
     return output
 
 

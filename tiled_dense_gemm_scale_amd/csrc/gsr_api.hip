@@ -14,10 +14,8 @@
 #include "gsr.h"
 #include "gsr_kernels.hpp"
 #include "gsr_pipeline.hpp"
-#include "gsr_bt.hpp"
 #include "gsr_interleave.hpp"
 #include "gsr_ksplit.hpp"
-#include "gsr_dual.hpp"
 #include "gsr_kspec.hpp"
 #include "gsr_interleave_h.hpp"
 #include "gsr_interleave_q.hpp"
@@ -60,13 +58,6 @@ hipError_t launch_pipe(const Problem& p, int grid, hipStream_t s)
                          dim3(gsr::kWave * WM * WN), s, p);
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_bt(const Problem& p, int grid, hipStream_t s)
-{
-    return launch_kernel((gsr::gemm_scale_relu_bt_kernel<BM, BN, WM, WN>), dim3(grid),
-                         dim3(gsr::kWave * WM * WN), s, p);
-}
-
 hipError_t launch_ilv(const Problem& p, int grid, hipStream_t s)
 {
     return launch_kernel(gsr::gemm_scale_relu_ilv_kernel, dim3(grid), dim3(gsr::IlvCfg::NT), s, p);
@@ -92,11 +83,6 @@ hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilvq_kernel, dim3(grid), dim3(256), s, p);
 }
 
-hipError_t launch_dual(const Problem& p, int grid, hipStream_t s)
-{
-    return launch_kernel(gsr::gemm_scale_relu_dual_kernel, dim3(grid), dim3(gsr::DualCfg::NT), s, p);
-}
-
 template <int BM, int BN, int S>
 hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
 {
@@ -111,8 +97,9 @@ hipError_t launch_kspec(const Problem& p, int grid, hipStream_t s)
 
 struct Entry {
     gsr_config cfg;
-    launch_fn vec;   // 128-bit path (16-byte aligned A/B, K and N multiples of 8)
-    launch_fn elem;  // element-wise path, any 2-byte aligned layout
+    launch_fn vec;       // 128-bit path (16-byte aligned A, B and C, K and N multiples of 8)
+    launch_fn elem;      // element-wise path, any 2-byte aligned layout
+    int elem_bm, elem_bn;  // the output tile of the element-wise kernel (its grid)
 };
 
 // Pipelined kernel: LDS ring of S stages filled by direct-to-LDS copies.  The
@@ -121,33 +108,17 @@ struct Entry {
     Entry                                                                                             \
     {                                                                                                 \
         {ID, BM, BN, BK, WM, WN, S, GROUP, 1, gsr::PipeCfg<BM, BN, BK, WM, WN, S>::LDS_BYTES},       \
-            launch_pipe<BM, BN, BK, WM, WN, S>, launch_staged<BM, BN, 64, WM, WN, false>              \
-    }
-// Register-staged kernel (two LDS buffers, global loads one step ahead in
-// registers, B transposed in registers).  stages = 0 marks this kind.
-#define GSR_STAGED(ID, BM, BN, WM, WN, GROUP)                                                         \
-    Entry                                                                                             \
-    {                                                                                                 \
-        {ID, BM, BN, 64, WM, WN, 0, GROUP, 1, gsr::TileKernel<BM, BN, 64, WM, WN, true>::LDS_BYTES}, \
-            launch_staged<BM, BN, 64, WM, WN, true>, launch_staged<BM, BN, 64, WM, WN, false>        \
-    }
-
-// A by direct-to-LDS copies, B transposed in registers: every operand read is
-// 128 bits.  stages = 1 marks this kind (two LDS buffers for each operand).
-#define GSR_BT(ID, BM, BN, WM, WN, GROUP)                                                             \
-    Entry                                                                                             \
-    {                                                                                                 \
-        {ID, BM, BN, 64, WM, WN, 1, GROUP, 1, gsr::BtCfg<BM, BN, WM, WN>::LDS_BYTES},                 \
-            launch_bt<BM, BN, WM, WN>, launch_staged<BM, BN, 64, WM, WN, false>                       \
+            launch_pipe<BM, BN, BK, WM, WN, S>, launch_staged<BM, BN, 64, WM, WN, false>, BM, BN      \
     }
 
 // Four waves splitting K inside the workgroup (block_k = 128 per step, waves
-// 1 x 1 over the output tile), LDS ring of S stages.
+// 1 x 1 over the output tile), LDS ring of S stages.  Element-wise path: the
+// 64x64 register-staged kernel.
 #define GSR_KSPLIT(ID, BM, BN, S, GROUP)                                                              \
     Entry                                                                                             \
     {                                                                                                 \
         {ID, BM, BN, 128, 1, 1, S, GROUP, 1, gsr::KsCfg<BM, BN, S>::LDS_BYTES},                       \
-            launch_ksplit<BM, BN, S>, launch_staged<64, 64, 64, 2, 2, false>                          \
+            launch_ksplit<BM, BN, S>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64                  \
     }
 
 // As GSR_KSPLIT with four more waves that only issue the copies, DEPTH steps
@@ -156,47 +127,55 @@ struct Entry {
     Entry                                                                                             \
     {                                                                                                 \
         {ID, BM, BN, 128, 1, 1, S, GROUP, 1, gsr::KsCfg<BM, BN, S>::LDS_BYTES},                       \
-            launch_kspec<BM, BN, S, D>, launch_staged<64, 64, 64, 2, 2, false>                        \
+            launch_kspec<BM, BN, S, D>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64                \
     }
 
-// The compiled tile table.  Tile choice per shape class is made by select().
+// An explicitly interleaved kernel (stages = 1: two LDS buffers per operand);
+// its element-wise path is the register-staged kernel of the same tile.
+#define GSR_ILV(ID, BM, BN, LDS, FN)                                                                   \
+    Entry                                                                                             \
+    {                                                                                                 \
+        {ID, BM, BN, 64, 2, 2, 1, 4, 1, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN       \
+    }
+
+// The compiled tile table, by id.  Ids are stable from one library version to
+// the next, so a tuning table written earlier keeps its meaning; the ids of
+// configurations that were dropped (0-4, 9, 11-14, 19, 20: tiles that neither
+// the selector nor any measured tuning entry chose) are not reused and are
+// rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is made
+// by select().
 const Entry kTable[] = {
-    GSR_PIPE(0, 256, 256, 64, 2, 4, 2, 4),   // 8 waves of 128x64, 2 x 64 KiB
-    GSR_PIPE(1, 256, 256, 32, 2, 4, 4, 4),   // 8 waves of 128x64, 4 x 32 KiB
-    GSR_PIPE(2, 256, 256, 32, 2, 4, 3, 4),   // 8 waves of 128x64, 3 x 32 KiB
-    GSR_PIPE(3, 256, 256, 64, 2, 2, 2, 4),   // 4 waves of 128x128
-    GSR_PIPE(4, 256, 256, 32, 2, 2, 4, 4),   // 4 waves of 128x128
     GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
     GSR_PIPE(6, 128, 256, 64, 2, 2, 3, 4),   // 4 waves of 64x128
     GSR_PIPE(7, 128, 128, 64, 2, 2, 4, 4),   // 4 waves of 64x64, 4 x 32 KiB
     GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
-    GSR_PIPE(9, 64, 64, 64, 2, 2, 8, 4),     // 4 waves of 32x32, 8 x 16 KiB
     GSR_PIPE(10, 64, 128, 64, 2, 2, 6, 4),   // 4 waves of 32x64
-    GSR_STAGED(11, 256, 256, 2, 4, 4),
-    GSR_STAGED(12, 128, 128, 2, 2, 4),
-    GSR_STAGED(13, 64, 64, 2, 2, 4),
-    GSR_BT(14, 256, 256, 2, 2, 4),           // 4 waves of 128x128
-    // explicit interleave, 4 waves of 128x128; stages = 1 as for GSR_BT
-    Entry{{15, 256, 256, 64, 2, 2, 1, 4, 1, gsr::IlvCfg::LDS_BYTES}, launch_ilv, launch_staged<256, 256, 64, 2, 2, false>},
+    // explicit interleave, 4 waves of 128x128 on 32x32x16 MFMAs
+    GSR_ILV(15, 256, 256, gsr::IlvCfg::LDS_BYTES, launch_ilv),
     GSR_KSPLIT(16, 64, 64, 4, 4),            // 4 waves split K, whole 64x64 tile each
     GSR_KSPLIT(17, 64, 32, 6, 4),
     GSR_KSPLIT(18, 32, 64, 6, 4),
-    GSR_KSPLIT(19, 64, 64, 5, 4),            // one more stage in flight (160 KiB)
-    // explicit interleave, both operands copied to LDS, B by transpose reads
-    Entry{{20, 256, 256, 64, 2, 2, 2, 4, 1, gsr::DualCfg::LDS_BYTES}, launch_dual, launch_staged<256, 256, 64, 2, 2, false>},
     // K split with separate copy waves (eight waves per workgroup), two steps ahead
     GSR_KSPEC(21, 64, 64, 4, 2, 4),
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
-    // explicit interleave at half height, 4 waves of 64x128; stages = 1 as for GSR_BT
-    Entry{{23, 128, 256, 64, 2, 2, 1, 4, 1, gsr::IlvHCfg::LDS_BYTES}, launch_ilvh, launch_staged<128, 256, 64, 2, 2, false>},
+    // explicit interleave at half height, 4 waves of 64x128
+    GSR_ILV(23, 128, 256, gsr::IlvHCfg::LDS_BYTES, launch_ilvh),
     // explicit interleave at a quarter of 256x256, 4 waves of 64x64
-    Entry{{24, 128, 128, 64, 2, 2, 1, 4, 1, gsr::IlvQCfg::LDS_BYTES}, launch_ilvq, launch_staged<128, 128, 64, 2, 2, false>},
+    GSR_ILV(24, 128, 128, gsr::IlvQCfg::LDS_BYTES, launch_ilvq),
     // config 15's tile and data flow on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave)
-    Entry{{25, 256, 256, 64, 2, 2, 1, 4, 1, gsr::Ilv16Cfg::LDS_BYTES}, launch_ilv16, launch_staged<256, 256, 64, 2, 2, false>},
+    GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16),
     // config 23's tile and data flow on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave)
-    Entry{{26, 128, 256, 64, 2, 2, 1, 4, 1, gsr::Ilv16HCfg::LDS_BYTES}, launch_ilv16h, launch_staged<128, 256, 64, 2, 2, false>},
+    GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
+
+// The table entry of a configuration id, or null for an id that is not compiled.
+const Entry* entry_of(int id)
+{
+    for (const Entry& e : kTable)
+        if (e.cfg.id == id) return &e;
+    return nullptr;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -259,7 +238,7 @@ int select(int64_t M, int64_t N, int64_t K)
         if ((copy_wave && K <= 256) || (four_wave && K > 256)) continue;
         if ((c.id == 15 && full_chip) || (c.id == 25 && !full_chip)) continue;
         if ((c.id == 23 && full_chip_h) || (c.id == 26 && !full_chip_h)) continue;
-        const gsr_config& g = kTable[c.id].cfg;
+        const gsr_config& g = entry_of(c.id)->cfg;
         const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
         const double full = std::floor(wgs / cus), fill = (wgs - full * cus) / cus;
         const double waves = full + (fill > 0.0 ? std::max(kPartMin, kPartA + (1.0 - kPartA) * fill) : 0.0);
@@ -289,7 +268,7 @@ std::atomic<bool> g_have_tuning{false};
 
 bool valid_launch(const Launch& l)
 {
-    return l.id >= 0 && l.id < kNumConfigs && l.group_m >= 1 && l.group_m <= 4096 &&
+    return entry_of(l.id) != nullptr && l.group_m >= 1 && l.group_m <= 4096 &&
            (l.xcd_remap == 0 || l.xcd_remap == 1);
 }
 
@@ -297,14 +276,14 @@ bool valid_launch(const Launch& l)
 // order; otherwise the tuning table, else the selector.
 Launch resolve(int64_t M, int64_t N, int64_t K, int config_id)
 {
-    if (config_id >= 0) return Launch{config_id, kTable[config_id].cfg.group_m, kTable[config_id].cfg.xcd_remap};
+    if (config_id >= 0) return Launch{config_id, entry_of(config_id)->cfg.group_m, entry_of(config_id)->cfg.xcd_remap};
     if (g_have_tuning.load(std::memory_order_acquire)) {
         std::lock_guard<std::mutex> lock(g_tune_mu);
         for (const Tuned& t : g_tuned)
             if (t.M == M && t.N == N && t.K == K) return t.l;
     }
     const int id = select(M, N, K);
-    return Launch{id, kTable[id].cfg.group_m, kTable[id].cfg.xcd_remap};
+    return Launch{id, entry_of(id)->cfg.group_m, entry_of(id)->cfg.xcd_remap};
 }
 
 struct DeviceInfo {
@@ -372,7 +351,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 500; }
+int gsr_version(void) { return 600; }
 
 const char* gsr_status_string(int status)
 {
@@ -390,11 +369,19 @@ const char* gsr_status_string(int status)
 
 int gsr_num_configs(void) { return kNumConfigs; }
 
+int gsr_config_ids(int32_t* ids, int32_t capacity)
+{
+    if (capacity < 0 || (ids == nullptr && capacity > 0)) return -1;
+    for (int i = 0; i < kNumConfigs && i < capacity; ++i) ids[i] = kTable[i].cfg.id;
+    return kNumConfigs;
+}
+
 int gsr_get_config(int32_t config_id, gsr_config* out)
 {
     if (out == nullptr) return GSR_ERROR_INVALID_VALUE;
-    if (config_id < 0 || config_id >= kNumConfigs) return GSR_ERROR_INVALID_CONFIG;
-    *out = kTable[config_id].cfg;
+    const Entry* e = entry_of(config_id);
+    if (e == nullptr) return GSR_ERROR_INVALID_CONFIG;
+    *out = e->cfg;
     return GSR_SUCCESS;
 }
 
@@ -402,7 +389,7 @@ int gsr_select_config(int64_t M, int64_t N, int64_t K, gsr_config* out)
 {
     if (out == nullptr || M < 0 || N < 0 || K < 0) return GSR_ERROR_INVALID_VALUE;
     const Launch l = resolve(M, N, K, -1);
-    *out = kTable[l.id].cfg;
+    *out = entry_of(l.id)->cfg;
     out->group_m = l.group_m;
     out->xcd_remap = l.xcd_remap;
     return GSR_SUCCESS;
@@ -427,7 +414,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
         if ((uintptr_t)bias & 1u) return GSR_ERROR_INVALID_VALUE;
         if (overlaps(bias, (uint64_t)N * 2u, C, (uint64_t)M * (uint64_t)N * 2u)) return GSR_ERROR_INVALID_VALUE;
     }
-    if (forced < -2 || forced >= kNumConfigs) return GSR_ERROR_INVALID_CONFIG;
+    if (forced < -2 || (forced >= 0 && entry_of(forced) == nullptr)) return GSR_ERROR_INVALID_CONFIG;
     if (forced == -2 && !valid_launch(given)) return GSR_ERROR_INVALID_CONFIG;
     if (M == 0 || N == 0) return GSR_SUCCESS;
     st = check_device();
@@ -443,7 +430,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     }
 
     const Launch l = (forced == -2) ? given : resolve(M, N, K, forced);
-    const Entry& e = kTable[l.id];
+    const Entry& e = *entry_of(l.id);
     Problem p;
     p.A = (const uint16_t*)A;
     p.B = (const uint16_t*)B;
@@ -454,14 +441,18 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     p.K = (int)K;
     p.alpha = alpha;
     p.act = (int)activation;
-    p.tiles_m = (int)cdiv(M, e.cfg.block_m);
-    p.tiles_n = (int)cdiv(N, e.cfg.block_n);
+    // The vector kernels read A and B and write C in 16-byte units (C's rows
+    // start 2N bytes apart, a multiple of 16 when N % 8 == 0) and read the
+    // bias in 8-byte units; anything else takes the element-wise kernel,
+    // whose own tile sets the grid.
+    const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
+                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 15u) == 0) &&
+                     (((uintptr_t)bias & 7u) == 0);
+    p.tiles_m = (int)cdiv(M, vec ? e.cfg.block_m : e.elem_bm);
+    p.tiles_n = (int)cdiv(N, vec ? e.cfg.block_n : e.elem_bn);
     p.group_m = l.group_m;
     p.xcd_remap = l.xcd_remap;
     const int grid = p.tiles_m * p.tiles_n;
-    const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
-                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 7u) == 0) &&
-                     (((uintptr_t)bias & 7u) == 0);
     const hipError_t err = (vec ? e.vec : e.elem)(p, grid, s);
     return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
 }

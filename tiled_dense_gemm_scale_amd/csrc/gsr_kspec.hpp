@@ -12,7 +12,10 @@
 // SIMD's MFMAs run while the other wave on it stalls on the memory path.
 // Every wave passes the same barriers, one per K-step t:
 //   copy wave:  wait until its copies of step t have landed; barrier t; send
-//               the copies of step t + DEPTH into the buffer step t - 1 used.
+//               the copies of step t + DEPTH into ring slot (t + DEPTH) %
+//               STAGES, the slot of step t + DEPTH - STAGES (step t - 2 in
+//               the compiled 4-slot, 2-deep form), whose reads every MFMA
+//               wave finished before barrier t - 1.
 //   MFMA wave:  barrier t (after its reads of step t - 1 have returned); read
 //               step t; MFMAs of step t - 1.
 // Tile, LDS operand layouts and the K split among the MFMA waves (wave w

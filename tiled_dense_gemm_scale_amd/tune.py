@@ -125,7 +125,7 @@ def tune_shape(gsr, text: str, top: int, min_gain: float, log) -> Dict:
         return rec
 
     # 1. every compiled configuration in its own launch order
-    for cid in range(gsr.num_configs()):
+    for cid in gsr.config_ids():
         cfg = gsr.get_config(cid)
         r = measure(cid, cfg["group_m"], cfg["xcd_remap"])
         log(f"[tune]   cfg {cid:2d} {r['tile']:>11s} {r['us']:9.2f} us {r['tflops']:8.1f} TF/s"
