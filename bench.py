@@ -100,17 +100,21 @@ def device_info(index: int) -> dict:
 
 
 class ClockSampler:
-    """The engine (graphics) clock the GPU reports while the timed calls run,
-    read through amdsmi in a background thread every `period_s` seconds.  The
-    part is power-limited under dense fp16 MFMA work, so this clock, not the
-    maximum the runtime reports, is what the achieved rate follows.  Sampling
-    only reads the driver's counters; any failure (no amdsmi, no permission,
-    the device not found) leaves the result None."""
+    """The engine (graphics) clock and the socket power the GPU reports while
+    the benchmark's calls run, read from the driver's metrics table through
+    amdsmi in a background thread.  The part is power-limited under dense fp16
+    MFMA work, so this clock, not the maximum the runtime reports, is what the
+    achieved rate follows.  The driver refreshes that table only about once a
+    second, so a reading is trusted only from `settle_s` seconds after the
+    sampling started (the caller keeps the GPU busy with the timed calls for
+    longer than that).  Each reading is the mean over the XCDs of their
+    current clocks.  Sampling only reads the driver's counters; any failure
+    (no amdsmi, no permission, the device not found) leaves the result None."""
 
-    def __init__(self, props, period_s: float = 0.004):
+    def __init__(self, props, period_s: float = 0.05, settle_s: float = 1.5):
         import threading
-        self.period_s = period_s
-        self.samples = []
+        self.period_s, self.settle_s = period_s, settle_s
+        self.samples = []  # (seconds since start, MHz, watts or None)
         self.error = None
         self._stop = threading.Event()
         self._thread = None
@@ -133,16 +137,23 @@ class ClockSampler:
             self.error = f"{type(e).__name__}: {e}"
 
     def _read(self):
-        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.SYS)
-        return float(info["clk"])
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float)) and v > 0]
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [float(m["current_gfxclk"])]
+        power = m.get("current_socket_power")
+        return (sum(clks) / len(clks) if clks else None), (float(power) if isinstance(power, (int, float)) else None)
 
     def _run(self):
+        t0 = time.perf_counter()
         while not self._stop.is_set():
             try:
-                self.samples.append(self._read())
+                mhz, watts = self._read()
             except Exception as e:  # noqa: BLE001
                 self.error = f"{type(e).__name__}: {e}"
                 return
+            if mhz is not None:
+                self.samples.append((time.perf_counter() - t0, mhz, watts))
             self._stop.wait(self.period_s)
 
     def start(self):
@@ -153,7 +164,7 @@ class ClockSampler:
         return self
 
     def stop(self):
-        """Median, min and max of the samples in MHz, or None."""
+        """Median, min and max of the settled readings, or None."""
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
@@ -162,11 +173,20 @@ class ClockSampler:
                 self._amdsmi.amdsmi_shut_down()
             except Exception:  # noqa: BLE001
                 pass
-        if not self.samples:
+        good = sorted(mhz for t, mhz, _ in self.samples if t >= self.settle_s)
+        watts = sorted(w for t, _, w in self.samples if t >= self.settle_s and w is not None)
+        if not good:
+            if self.error is None:
+                self.error = f"no reading after the first {self.settle_s} s"
             return None
-        v = sorted(self.samples)
-        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
-                "source": "amdsmi graphics clock, sampled every ~4 ms while the timed graph and its repeats ran"}
+        out = {"median_mhz": round(good[len(good) // 2], 1), "min_mhz": round(good[0], 1),
+               "max_mhz": round(good[-1], 1), "samples": len(good)}
+        if watts:
+            out["socket_power_w"] = watts[len(watts) // 2]
+        out["source"] = ("amdsmi metrics table (mean over XCDs of the current graphics clock), read every "
+                         f"{self.period_s * 1e3:.0f} ms while the timed calls were replayed for the clock window; "
+                         f"readings from the first {self.settle_s} s dropped (the table refreshes about once a second)")
+        return out
 
 
 def time_graph(graph, stream, steps: int, repeats: int):
@@ -283,6 +303,9 @@ def main(argv=None) -> int:
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra replays of the timed graph for median/min (graph launch only)")
     ap.add_argument("--no-context", action="store_true", help="skip the dispatch-floor measurement")
+    ap.add_argument("--clock-window-s", type=float, default=3.0,
+                    help="seconds of the same calls, after the timed region, during which the engine clock and "
+                         "socket power are sampled (0: skip)")
     ap.add_argument("--no-torch-context", action="store_true",
                     help="skip timing torch's unfused matmul -> mul -> relu and its plain fp16 matmul")
     ap.add_argument("--cold", action="store_true",
@@ -354,9 +377,7 @@ def main(argv=None) -> int:
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    clock = ClockSampler(props)
     torch.cuda.synchronize()  # single rank: the barrier is this synchronise
-    clock.start()
     start.record(stream)
     if graph is not None:
         with torch.cuda.stream(stream):
@@ -385,12 +406,28 @@ def main(argv=None) -> int:
         context["repeat_ms_per_step"] = {"median": round(reps[len(reps) // 2], 6), "min": round(reps[0], 6),
                                          "max": round(reps[-1], 6), "n": len(reps)}
         log(f"[bench] repeats: {context['repeat_ms_per_step']}")
-    observed = clock.stop()
-    context["engine_clock_observed"] = observed
-    if observed is None:
-        log(f"[bench] engine clock not sampled ({clock.error})")
-    else:
-        log(f"[bench] engine clock while timed: {observed}")
+    if args.clock_window_s > 0:
+        # The same calls again for a few seconds (the timed graph replayed, or
+        # the eager calls), while the driver's clock and power readings are
+        # sampled; outside the timed region.
+        clock = ClockSampler(props)
+        torch.cuda.synchronize()
+        clock.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.clock_window_s:
+            with torch.cuda.stream(stream):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    for _ in range(args.steps):
+                        step()
+            torch.cuda.synchronize()
+        observed = clock.stop()
+        context["engine_clock_observed"] = observed
+        if observed is None:
+            log(f"[bench] engine clock not sampled ({clock.error})")
+        else:
+            log(f"[bench] engine clock under the timed calls: {observed}")
     if graph is not None and not args.no_context:
         a0 = torch.empty((1, 0), dtype=torch.float16, device=dev)
         b0 = torch.empty((0, 8), dtype=torch.float16, device=dev)
@@ -444,12 +481,30 @@ def main(argv=None) -> int:
                 cold.append((e0, e1))
         torch.cuda.synchronize()
         cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in cold)[len(cold) // 2]
+        # the same single eager calls with the caches left warm (a small
+        # kernel instead of the flush before each), so the cold penalty can be
+        # told apart from the cost of timing one dispatch on its own
+        warm = []
+        with torch.cuda.stream(stream):
+            for i in range(len(cold)):
+                sink[:4096].fill_(float(i))  # a small kernel before the call, as in the cold loop
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step()
+                e1.record(stream)
+                warm.append((e0, e1))
+        torch.cuda.synchronize()
+        warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in warm)[len(warm) // 2]
         del flush, clean, sink
         torch.cuda.empty_cache()
         context["cold_us_per_call"] = round(cold_ms * 1e3, 3)
         context["cold_tflops"] = round(w.flops / (cold_ms * 1e-3) / 1e12, 3)
+        context["warm_single_call_us"] = round(warm_ms * 1e3, 3)
+        if w.flops / w.algorithmic_bytes < PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            context["cold_hbm_gbs_algorithmic"] = round(w.algorithmic_bytes / (cold_ms * 1e-3) / 1e9, 1)
         log(f"[bench] cold caches (median of {len(cold)}): {cold_ms * 1e3:.2f} us/call "
-            f"({context['cold_tflops']} TFLOP/s)")
+            f"({context['cold_tflops']} TFLOP/s); warm single calls {warm_ms * 1e3:.2f} us/call")
     if graph is not None and args.zero_input:
         za = torch.zeros_like(a)
         zb = torch.zeros_like(b)

@@ -64,8 +64,11 @@ enum gsr_activation {
  * MFMAs, all others from 32x32x16 fp16 MFMAs.  (The K-split kinds, block_k
  * 128 with waves 1 x 1, give every wave the whole tile and a share of each
  * K-step instead.)  group_m is the number of tile rows in one group of the
- * grouped launch order, xcd_remap says whether workgroup ids are regrouped so
- * that neighbouring tiles run on the same XCD.  Ids are stable across library
+ * grouped launch order; xcd_remap picks how workgroup ids map to tiles: 0 the
+ * grouped order on the ids as dispatched, 1 the same on ids regrouped so that
+ * neighbouring tiles run on the same XCD, 2 chip-wide rounds of 16 x 16 tiles
+ * with a 4 x 8 part per XCD (grids whose tile rows and columns are multiples
+ * of 16; others use 1; group_m unused).  Ids are stable across library
  * versions and not contiguous: gsr_config_ids lists the compiled ones. */
 typedef struct gsr_config {
     int32_t id;
@@ -123,7 +126,7 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K,
 
 /* As gemm_scale_bias_act with an explicit launch: cfg->id picks the compiled
  * tile configuration; cfg->group_m (1..4096, tile rows per group of the
- * launch order) and cfg->xcd_remap (0 or 1) override that configuration's
+ * launch order) and cfg->xcd_remap (0, 1 or 2) override that configuration's
  * launch order; the other fields are ignored.  The launch order changes only
  * which tiles run together, never a tile's arithmetic, so results are bit
  * for bit those of gemm_scale_bias_act_ex with the same id.  For tuning

@@ -189,7 +189,7 @@ def test_tuning_table_host_side(native, tmp_path):
         for bad in ("1024 1024 1024 99 1 0\n",      # unknown config id
                     "1024 1024 1024 9 1 0\n",       # a retired config id
                     "1024 1024 1024 7 0 0\n",       # group_m < 1
-                    "1024 1024 1024 7 1 2\n",       # xcd_remap not 0/1
+                    "1024 1024 1024 7 1 3\n",       # xcd_remap not 0, 1 or 2
                     "1024 1024 7 1 0\n",            # too few fields
                     "1024 1024 1024 7 1 0 5\n",     # too many fields
                     "-1 4 4 7 1 0\n",               # negative size
@@ -209,7 +209,7 @@ def test_tuning_table_host_side(native, tmp_path):
 
 def test_launch_entry_point_checks(native):
     # explicit launches are validated on the host before any device work
-    for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (7, 0, 1), (7, 5000, 1), (7, 4, 2)):
+    for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (7, 0, 1), (7, 5000, 1), (7, 4, 3), (7, 4, -1), (9, 4, 1)):
         st = native.gemm_scale_bias_act_cfg(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 0, 0, cid, gm, xcd)
         assert st == 6, (cid, gm, xcd, st)
 

@@ -24,9 +24,16 @@ def gsr(native):
     g.clear_tuning()
 
 
-@pytest.mark.parametrize("cid", [15, 16, 7, 18, 21, 22, 24, 25, 26])
-def test_launch_order_does_not_change_results(gsr, orc, cid):
-    M, N, K = 700, 1100, 264
+@pytest.mark.parametrize("cid,shape", [(15, (700, 1100, 264)), (16, (700, 1100, 264)), (7, (700, 1100, 264)),
+                                       (18, (700, 1100, 264)), (21, (700, 1100, 264)), (22, (700, 1100, 264)),
+                                       (24, (700, 1100, 264)), (25, (700, 1100, 264)), (26, (700, 1100, 264)),
+                                       (25, (4096, 4096, 136)), (25, (8192, 4096, 72)), (15, (4096, 8192, 72))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_launch_order_does_not_change_results(gsr, orc, cid, shape):
+    """Every launch order, including the chip rounds of 16 x 16 tiles (order 2,
+    active on the 4096- and 8192-wide grids of 256 x 256 tiles), gives the
+    compiled order's bits; the compiled order matches the oracle."""
+    M, N, K = shape
     a, b = W.normal_inputs(M, N, K, seed=cid)
     ad, bd = a.to(DEV), b.to(DEV)
     ref = gsr.gemm_scale_relu_ex(ad, bd, 0.5, cid).clone()
@@ -34,7 +41,7 @@ def test_launch_order_does_not_change_results(gsr, orc, cid):
     oref, _ = orc.gemm_scale_relu(W.fp16_bits(a), W.fp16_bits(b), 0.5)
     PT.assert_parity(f"cfg{cid} default order", W.fp16_bits(ref.cpu()), oref)
     for gm in (1, 2, 3, 8, 64):
-        for xcd in (0, 1):
+        for xcd in (0, 1, 2):
             print(f"[gpu] launch order cfg {cid} group {gm} xcd {xcd}", flush=True)
             out = gsr.gemm_launch(ad, bd, 0.5, cid, gm, xcd)
             torch.cuda.synchronize()

@@ -132,10 +132,10 @@ struct Entry {
 
 // An explicitly interleaved kernel (stages = 1: two LDS buffers per operand);
 // its element-wise path is the register-staged kernel of the same tile.
-#define GSR_ILV(ID, BM, BN, LDS, FN)                                                                   \
+#define GSR_ILV(ID, BM, BN, LDS, FN, XCD)                                                              \
     Entry                                                                                             \
     {                                                                                                 \
-        {ID, BM, BN, 64, 2, 2, 1, 4, 1, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN       \
+        {ID, BM, BN, 64, 2, 2, 1, 4, XCD, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN     \
     }
 
 // The compiled tile table, by id.  Ids are stable from one library version to
@@ -151,7 +151,7 @@ const Entry kTable[] = {
     GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
     GSR_PIPE(10, 64, 128, 64, 2, 2, 6, 4),   // 4 waves of 32x64
     // explicit interleave, 4 waves of 128x128 on 32x32x16 MFMAs
-    GSR_ILV(15, 256, 256, gsr::IlvCfg::LDS_BYTES, launch_ilv),
+    GSR_ILV(15, 256, 256, gsr::IlvCfg::LDS_BYTES, launch_ilv, 1),
     GSR_KSPLIT(16, 64, 64, 4, 4),            // 4 waves split K, whole 64x64 tile each
     GSR_KSPLIT(17, 64, 32, 6, 4),
     GSR_KSPLIT(18, 32, 64, 6, 4),
@@ -159,13 +159,14 @@ const Entry kTable[] = {
     GSR_KSPEC(21, 64, 64, 4, 2, 4),
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
     // explicit interleave at half height, 4 waves of 64x128
-    GSR_ILV(23, 128, 256, gsr::IlvHCfg::LDS_BYTES, launch_ilvh),
+    GSR_ILV(23, 128, 256, gsr::IlvHCfg::LDS_BYTES, launch_ilvh, 1),
     // explicit interleave at a quarter of 256x256, 4 waves of 64x64
-    GSR_ILV(24, 128, 128, gsr::IlvQCfg::LDS_BYTES, launch_ilvq),
-    // config 15's tile and data flow on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave)
-    GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16),
+    GSR_ILV(24, 128, 128, gsr::IlvQCfg::LDS_BYTES, launch_ilvq, 1),
+    // config 15's tile and data flow on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave);
+    // chip rounds of 16 x 16 tiles where the grid divides into them
+    GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16, 2),
     // config 23's tile and data flow on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave)
-    GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h),
+    GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -269,7 +270,7 @@ std::atomic<bool> g_have_tuning{false};
 bool valid_launch(const Launch& l)
 {
     return entry_of(l.id) != nullptr && l.group_m >= 1 && l.group_m <= 4096 &&
-           (l.xcd_remap == 0 || l.xcd_remap == 1);
+           l.xcd_remap >= 0 && l.xcd_remap <= 2;
 }
 
 // The launch for a problem: a forced config id keeps its compiled launch

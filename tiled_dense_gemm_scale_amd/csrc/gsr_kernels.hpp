@@ -199,8 +199,29 @@ __device__ __forceinline__ void with_activation(int act, F&& f)
 }
 
 // Workgroup id -> (tile row, tile column).
+//  xcd_remap 0: grouped order on the workgroup ids as dispatched.
+//  xcd_remap 1: the same on ids regrouped so that each XCD gets a contiguous
+//    range of them (consecutive tiles share an XCD's L2).
+//  xcd_remap 2: chip rounds of 16 x 16 tiles, for grids that divide into
+//    them (otherwise as 1): workgroups go to the 8 XCDs round-robin and an
+//    XCD's 32 CUs run its workgroups 32 at a time, so slot s of XCD x runs in
+//    round s / 32; in every round the chip covers one 16 x 16 block of tiles,
+//    XCD x a 4 x 8 part of it (rows 4 (x / 2) .., columns 8 (x % 2) ..).
+//    Each XCD's L2 still needs 4 A and 8 B panels per round, as in order 1,
+//    but the chip as a whole needs 16 + 16 panels from HBM per round instead
+//    of 32 + 8 (in order 1 every XCD holds its own tile rows).  group_m is
+//    not used.  At 16384^3 with 256 x 256 tiles this measured 0.9 % faster
+//    than order 1 (interleaved timings on one MI355X).
 __device__ __forceinline__ void tile_of(int pid, int nwg, const Problem& p, int& tm, int& tn)
 {
+    if (p.xcd_remap == 2 && (p.tiles_m & 15) == 0 && (p.tiles_n & 15) == 0) {
+        const int x = pid & 7, s = pid >> 3;  // XCD, slot in its dispatch order
+        const int r = s >> 5, j = s & 31;     // round, tile of the round on this XCD
+        const int per_row = p.tiles_n >> 4;   // 16 x 16 blocks per block row
+        tm = (r / per_row) * 16 + (x >> 1) * 4 + (j & 3);
+        tn = (r % per_row) * 16 + (x & 1) * 8 + (j >> 2);
+        return;
+    }
     if (p.xcd_remap) {
         // Workgroups are handed to the 8 XCDs round-robin: give XCD x a
         // contiguous range of logical ids instead.

@@ -108,11 +108,27 @@ __device__ __forceinline__ uint32_t swz_a(uint32_t r)
 }
 
 // B tile rows (one k each) of BN halves: chunk c of row k sits at c ^ swz_b(k).
-// Four consecutive rows get XOR masks whose bits 1-2 and bits 2-3 are both
-// distinct, which spreads a transpose read's 4 rows x 2-4 chunks over all banks.
+// A transpose read hands each 16-lane group rows k..k+3 of a 16-k substep
+// (k = 8g' + 4r, g' = lane group / 2) and two 16-byte chunks per row, the
+// group next to it the next two chunks of the same rows.
+//  * 128-byte rows (BN = 64): the LDS serves 64 banks of 4 bytes per cycle,
+//    so even rows fall on one half of the banks and odd rows on the other, and
+//    rows k and k + 8 are read by the same instruction.  Masks (2(k mod 4)) ^
+//    (2 if k mod 16 >= 8) give the rows served together disjoint chunks
+//    whether the cycle takes lanes 0-31 (rows k..k+3, four chunks each) or
+//    lanes 0-15 with 32-47 (rows k..k+3 and k+8..k+11, two chunks each), and
+//    also when 16 lanes are served per cycle.  The masks 0, 6, 2, 4 by
+//    k mod 4 used before repeat every four rows, which left rows k and k + 2
+//    (and k and k + 8) on the same banks: two extra cycles per read
+//    (rocprofv3 SQ_LDS_BANK_CONFLICT, one cycle per LDS instruction on the
+//    64x64 K-split kernel at 1024^3).
+//  * other widths: four consecutive rows get XOR masks whose bits 1-2 and
+//    bits 2-3 are both distinct, which spreads a read's 4 rows x 2-4 chunks
+//    over the banks.
 template <int CHN>
 __device__ __forceinline__ uint32_t swz_b(uint32_t k)
 {
+    if constexpr (CHN == 8) return ((k & 3u) << 1) ^ ((k >> 2) & 2u);
     const uint32_t e = k & 3u;
     const uint32_t f = ((e & 1u) * 6u) ^ ((e >> 1) * 10u);  // 0, 6, 10, 12
     return f & (uint32_t)(CHN - 1);

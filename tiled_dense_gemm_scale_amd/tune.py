@@ -136,18 +136,20 @@ def tune_shape(gsr, text: str, top: int, min_gain: float, log) -> Dict:
     for cid in best_ids:
         base = gsr.gemm_launch(a, b, alpha, cid, gsr.get_config(cid)["group_m"],
                                gsr.get_config(cid)["xcd_remap"]).clone()
-        for gm in GROUPS:
-            for xcd in (0, 1):
-                cfg = gsr.get_config(cid)
-                if gm == cfg["group_m"] and xcd == cfg["xcd_remap"]:
-                    continue
-                r = measure(cid, gm, xcd)
-                same = torch.equal(c.view(torch.int16), base.view(torch.int16))
-                r["bitwise_equal_to_default_order"] = same
-                if not same:
-                    r["matches_selector_output"] = False
-                log(f"[tune]   cfg {cid:2d} group {gm:2d} xcd {xcd} {r['us']:9.2f} us"
-                    f"{'' if same else '  ORDER CHANGED THE RESULT'}")
+        cfg = gsr.get_config(cid)
+        orders = [(gm, xcd) for gm in GROUPS for xcd in (0, 1)]
+        if -(-M // cfg["block_m"]) % 16 == 0 and -(-N // cfg["block_n"]) % 16 == 0:
+            orders.append((cfg["group_m"], 2))  # chip rounds of 16 x 16 tiles (group_m unused)
+        for gm, xcd in orders:
+            if gm == cfg["group_m"] and xcd == cfg["xcd_remap"]:
+                continue
+            r = measure(cid, gm, xcd)
+            same = torch.equal(c.view(torch.int16), base.view(torch.int16))
+            r["bitwise_equal_to_default_order"] = same
+            if not same:
+                r["matches_selector_output"] = False
+            log(f"[tune]   cfg {cid:2d} group {gm:2d} xcd {xcd} {r['us']:9.2f} us"
+                f"{'' if same else '  ORDER CHANGED THE RESULT'}")
 
     valid = [r for r in cands if r["matches_selector_output"]]
     best = min(valid, key=lambda r: r["us"])
