@@ -39,7 +39,7 @@ def test_config_struct_layout(native):
 
 
 # Ids of configurations dropped from the table; they are never reused.
-RETIRED_IDS = (0, 1, 2, 3, 4, 9, 11, 12, 13, 14, 19, 20)
+RETIRED_IDS = (0, 1, 2, 3, 4, 9, 11, 12, 13, 14, 15, 19, 20)
 
 
 def test_config_table(native):
@@ -179,14 +179,14 @@ def test_tuning_table_host_side(native, tmp_path):
     base = native.select_config(1024, 1024, 1024)
     other = native.select_config(1024, 1024, 1025)
     good = tmp_path / "t.txt"
-    good.write_text("# comment line\n\n1024 1024 1024 7 2 0   # trailing comment\n300 520 200 15 8 1\n")
+    good.write_text("# comment line\n\n1024 1024 1024 7 2 0   # trailing comment\n300 520 200 28 8 1\n")
     native.load_tuning(str(good))
     try:
         assert native.tuning_entries() == 2
         c = native.select_config(1024, 1024, 1024)
         assert (c["id"], c["group_m"], c["xcd_remap"]) == (7, 2, 0)
         c = native.select_config(300, 520, 200)
-        assert (c["id"], c["group_m"], c["xcd_remap"]) == (15, 8, 1)
+        assert (c["id"], c["group_m"], c["xcd_remap"]) == (28, 8, 1)
         assert native.select_config(1024, 1024, 1025) == other  # not in the table
         for bad in ("1024 1024 1024 99 1 0\n",      # unknown config id
                     "1024 1024 1024 9 1 0\n",       # a retired config id

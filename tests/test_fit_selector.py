@@ -14,10 +14,10 @@ API = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc", "gsr_api.hip")
 
 def test_fit_recovers_a_known_model():
     """Times generated from known rates and fixed costs are fitted back."""
-    tiles = {15: (256, 256), 23: (128, 256), 24: (128, 128), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128), 8: (128, 64),
-             25: (256, 256), 26: (128, 256), 21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
+    tiles = {28: (256, 256), 23: (128, 256), 24: (128, 128), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128),
+             8: (128, 64), 26: (128, 256), 21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
     truth = {cid: (1.0 + 0.5 * i, 2.0 + 0.25 * i) for i, cid in enumerate(sorted(tiles))}
-    a, pmin, full = 0.2, 0.6, (96, 160)
+    a, pmin, full = 0.2, 0.6, (160,)
     times = {}
     for M in (16, 200, 1000, 4100, 8200):
         for N in (512, 3000, 11008):
@@ -33,17 +33,17 @@ def test_fit_recovers_a_known_model():
     assert mean == pytest.approx(1.0) and worst == pytest.approx(1.0)
 
 
-def test_full_chip_rules_swap_the_256_and_128x256_tile_kernels():
-    f = (160, 192)
-    assert 15 in F.candidates(1024, 4096, 4096, f) and 25 not in F.candidates(1024, 4096, 4096, f)
-    assert 25 in F.candidates(4096, 4096, 4096, f) and 15 not in F.candidates(4096, 4096, 4096, f)
-    assert F.workgroups((256, 256), 2560, 4096) == 160 and 25 in F.candidates(2560, 4096, 4096, f)
-    assert 15 in F.candidates(2304, 4096, 4096, f)  # 9 x 16 = 144 tiles
-    assert 25 in F.candidates(2305, 4000, 4096, f)  # a ragged tenth tile row: 10 x 16 = 160 tiles
-    # the 128x256 pair: 2048 x 4096 is 16 x 16 = 256 tiles, 1408 x 4096 is 11 x 16 = 176
+def test_full_chip_rule_swaps_the_128x256_tile_kernels():
+    f = (176,)
+    # one 256x256 kernel at every grid size
+    for M, N in ((1024, 4096), (4096, 4096), (16, 11008), (2304, 4096)):
+        assert 28 in F.candidates(M, N, 4096, f) and 15 not in F.candidates(M, N, 4096, f)
+        assert 25 not in F.candidates(M, N, 4096, f)
+    # the 128x256 pair: 2048 x 4096 is 16 x 16 = 256 tiles, 1408 x 4096 is 11 x 16 = 176, 1280 x 4096 160
     assert 26 in F.candidates(2048, 4096, 4096, f) and 23 not in F.candidates(2048, 4096, 4096, f)
-    assert 23 in F.candidates(1408, 4096, 4096, f) and 26 not in F.candidates(1408, 4096, 4096, f)
-    assert 23 in F.candidates(2048, 4096, 4096, (160, F.NEVER))
+    assert 26 in F.candidates(1408, 4096, 4096, f) and 23 not in F.candidates(1408, 4096, 4096, f)
+    assert 23 in F.candidates(1280, 4096, 4096, f) and 26 not in F.candidates(1280, 4096, 4096, f)
+    assert 23 in F.candidates(2048, 4096, 4096, (F.NEVER,))
     assert F.candidates(16, 11008, 256, f)[-2:] == F.FOUR_WAVE and F.candidates(16, 11008, 257, f)[-2:] == F.COPY_WAVE
 
 
@@ -71,8 +71,8 @@ def test_selector_table_is_the_fit_of_the_committed_measurements():
         assert tile_us == pytest.approx(params[cid][1], abs=0.006), cid
     consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
     assert float(consts.group(1)) == pytest.approx(pmin) and float(consts.group(2)) == pytest.approx(a)
-    assert int(re.search(r"kFullChipTiles = (\d+);", src).group(1)) == full[0]
-    assert int(re.search(r"kFullChipTilesH = (\d+);", src).group(1)) == full[1]
+    assert re.search(r"kFullChipTiles = ", src) is None  # one 256x256 kernel, no rule
+    assert int(re.search(r"kFullChipTilesH = (\d+);", src).group(1)) == full[0]
     assert mean < 1.005 and worst < 1.05
 
 
@@ -81,18 +81,12 @@ def test_library_selector_matches_the_model(native):
     times, tiles = F.load(CSV)
     src = open(API).read()
     consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
-    full = int(re.search(r"kFullChipTiles = (\d+);", src).group(1))
     full_h = int(re.search(r"kFullChipTilesH = (\d+);", src).group(1))
     mean, worst, a, pmin, full, params = F.fit(times, tiles, a_grid=np.array([float(consts.group(2))]),
-                                               p_grid=np.array([float(consts.group(1))]), full_grid=(full,),
-                                               full_h_grid=(full_h,))
-    # select() hands the model's config 25 to its successor (same tile and
-    # bits, B copied to LDS instead of transposed through registers)
-    successor = int(re.search(r"kSuccessorOf25 = (\d+);", src).group(1))
+                                               p_grid=np.array([float(consts.group(1))]), full_h_grid=(full_h,))
     disagree = []
     for (M, N, K), t in times.items():
         want = F.choose(params, tiles, M, N, K, a, pmin, full)
-        want = successor if want == 25 else want
         got = native.select_config(M, N, K)["id"]
         if got != want:
             disagree.append(((M, N, K), got, want))

@@ -1,16 +1,20 @@
 // gsr_interleave16.hpp -- the 256x256 explicitly interleaved kernel on the
-// 16x16x32 fp16 MFMA.
+// 16x16x32 fp16 MFMA with B transposed through registers (configuration 25),
+// and the 16x16x32 fragment MFMA and epilogue that the kernel of
+// gsr_interleave16d.hpp (configuration 28, B copied to LDS and read with
+// transpose reads) shares.  The selector runs configuration 28, which gives
+// this kernel's bits faster; this one is kept as its register-transpose twin.
 //
-// Same tile, waves, LDS stages, global traffic and one-barrier-per-K-step
-// structure as the 32x32x16 kernel in gsr_interleave.hpp; what changes is the
-// matrix instruction and with it the operand fragments, the unit plan and the
-// accumulator layout.  Why: with random fp16 operands the part runs
-// power-limited, and a chip-wide stream of v_mfma_f32_16x16x32_f16 holds a
-// markedly higher engine clock than the same FLOP issued as
-// v_mfma_f32_32x32x16_f16 (both at their full issue rate: ~1.7-1.8 vs
-// ~1.4-1.5 GHz), so where enough CUs run for that limit to bind it finishes
-// the same work sooner even though its 16-cycle MFMAs leave half the issue
-// shadow for the other instructions of a K-step.
+// The 256x256 tile of the interleave design (gsr_interleave.hpp): four waves
+// of 128x128, two LDS stages, A copied straight into LDS, B loaded into
+// registers one 8x8 block per thread, transposed with byte permutes and
+// written K-contiguous, one barrier per K-step.  Why 16x16x32 MFMAs: with
+// random fp16 operands the part runs power-limited, and a chip-wide stream of
+// v_mfma_f32_16x16x32_f16 holds a markedly higher engine clock than the same
+// FLOP issued as v_mfma_f32_32x32x16_f16 (both at their full issue rate:
+// ~1.7-1.8 vs ~1.4-1.5 GHz), so where enough CUs run for that limit to bind
+// it finishes the same work sooner even though its 16-cycle MFMAs leave half
+// the issue shadow for the other instructions of a K-step.
 //
 // Each wave owns 128x128 of the tile as 8 x 8 accumulator blocks of 16x16
 // (four fp32 per lane each, all 256 in AGPRs).  A K-step (BK = 64) is two
@@ -151,7 +155,7 @@ gemm_scale_relu_ilv16_kernel(Problem p)
     const uint32_t K = (uint32_t)p.K, N = (uint32_t)p.N;
     const uint32_t lds0 = lds_address(smem);
 
-    // ---- descriptors that advance along K (as in the 32x32x16 kernel) ------
+    // ---- descriptors that advance along K -----------------------------------
     uint64_t a_base = (uint64_t)(uintptr_t)p.A + ((uint64_t)m0 * K) * 2u;
     uint32_t a_recs = ((uint32_t)p.M * K - (uint32_t)m0 * K) * 2u;
     uint64_t b_base = (uint64_t)(uintptr_t)p.B + (uint64_t)n0 * 2u;
@@ -170,8 +174,8 @@ gemm_scale_relu_ilv16_kernel(Problem p)
     };
 
     // ---- per-lane copy plan --------------------------------------------------
-    // The 32x32x16 kernel's plan, kept in a few base registers: a 256-thread
-    // tile has no room for eight-entry offset tables beside the operand sets.
+    // Kept in a few base registers: a 256-thread tile has no room for
+    // eight-entry offset tables beside the operand sets.
     // A copy i of this wave fills LDS chunk positions 64*(wave+4i) + lane: row
     // r = 8*wave + 32i + lane/8, physical chunk lane % 8, logical chunk
     // c = (lane % 8) ^ swz(r) = c0 ^ 4*(i & 1) with c0 below.

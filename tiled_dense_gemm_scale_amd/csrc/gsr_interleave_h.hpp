@@ -3,8 +3,8 @@
 // tiles leave CUs idle (e.g. 2048 x 4096 x 4096: 256 tiles of 128x256, 128 of
 // 256x256).
 //
-// The structure is that of the 256x256 kernel (gsr_interleave.hpp) at half
-// the tile height: four waves, each owning 64x128 of the tile (2 x 4
+// The interleave design of gsr_interleave.hpp on a 128x256 tile: four
+// waves, each owning 64x128 of the tile (2 x 4
 // accumulator blocks, 128 fp32 accumulators per lane), two LDS stages (A
 // 16 KiB + B 32 KiB each), A copied straight into LDS, B loaded into registers
 // as one 8x8 block per thread, transposed with byte permutes and written
@@ -18,10 +18,10 @@
 //              write per unit into the other stage;
 //   substep 3: the wait + barrier after unit 1, then the 6 substep-0 reads of
 //              step t+1 on units 2-7 and the 4 A(t+2) copies on units 2-5.
-// The LDS carries 144 KiB per K-step per CU against 1024 MFMA cycles (the
-// 256x256 kernel: 192 KiB against 2048), so this tile is LDS-bound rather than
+// The LDS carries 144 KiB per K-step per CU against 1024 MFMA cycles (a
+// 256x256 tile: 192 KiB against 2048), so this tile is LDS-bound rather than
 // MFMA-bound; it pays where it fills the chip and 256x256 does not.
-// Ragged edges as in the 256x256 kernel.
+// Ragged edges as in gsr_interleave.hpp.
 #pragma once
 
 #include "gsr_interleave.hpp"

@@ -3,8 +3,8 @@
 // 128x128 tiles (e.g. 1024 x 4096 x 4096: 256 tiles of 128x128, 128 of
 // 128x256, 64 of 256x256).
 //
-// The structure of the 256x256 and 128x256 kernels (gsr_interleave.hpp,
-// gsr_interleave_h.hpp) at a quarter of the 256x256 tile: four waves, each
+// The interleave design of gsr_interleave.hpp (and of the 128x256 kernel in
+// gsr_interleave_h.hpp) on a 128x128 tile: four waves, each
 // owning 64x64 of the tile (2 x 2 accumulator blocks), two LDS stages (A and B
 // 16 KiB each), A copied straight into LDS (4 copies per wave per step), every
 // operand read 128 bits wide, both operands requested two K-steps ahead, one
@@ -20,7 +20,7 @@
 //              reads and the 4 A(t+2) copies on units 1-3.
 // LDS carries 96 KiB per K-step per CU against 512 MFMA cycles, so this tile
 // is LDS-bound (the operand reads per MFMA double against 256x256); it pays
-// where larger tiles leave CUs idle.  Ragged edges as in the 256x256 kernel.
+// where larger tiles leave CUs idle.  Ragged edges as in gsr_interleave.hpp.
 #pragma once
 
 #include "gsr_interleave.hpp"

@@ -6,17 +6,18 @@ The selector in csrc/gsr_api.hip prices a candidate tile bm x bn as
 
 with wgs = ceil(M / bm) * ceil(N / bn) workgroups on 256 CUs and
 waves(wgs) = full waves + (a part-filled last wave: max(pmin, a + (1 - a) * fill)).
-The 256x256 and 128x256 tiles have two kernels each: one on 32x32x16 MFMAs
-(configs 15 and 23, the higher issue efficiency) and one on 16x16x32 MFMAs
-(configs 25 and 26, the higher engine clock once enough CUs run for the power
-limit to bind); config 25 stands in for config 15 when the 256x256 grid has
-at least full[0] workgroups, config 26 for config 23 when the 128x256 grid has
-at least full[1].  This module fits `rate` (TFLOP/s per CU) and `tile_us` per
-configuration by least squares in relative error on the shapes where it is a
-candidate, and picks (a, pmin, full) on grids whose choices come closest to
-the fastest measured configuration (mean log ratio): first (full[0], a, pmin)
-with config 26 left out, then full[1], then (a, pmin) again.  Input: the CSV written from a `tune.py --top 0` report
-(tuning/mi355x_config_times.csv) or such a JSON report itself.
+The 256x256 tile has one kernel (config 28, 16x16x32 MFMAs with B copied to
+LDS: measured faster than both other 256x256 kernels on every one of the 60
+shapes).  The 128x256 tile has two: config 23 on 32x32x16 MFMAs (the higher
+issue efficiency) and config 26 on 16x16x32 MFMAs (the higher engine clock
+once enough CUs run for the power limit to bind); config 26 stands in for
+config 23 when the 128x256 grid has at least full[0] workgroups.  This module
+fits `rate` (TFLOP/s per CU) and `tile_us` per configuration by least squares
+in relative error on the shapes where it is a candidate, and picks (a, pmin,
+full) on grids whose choices come closest to the fastest measured
+configuration (mean log ratio): first (a, pmin) with config 26 left out, then
+full[0], then (a, pmin) again.  Input: the CSV written from a `tune.py --top 0`
+report (tuning/mi355x_config_times.csv) or such a JSON report itself.
 
     python -m tiled_dense_gemm_scale_amd.fit_selector tuning/mi355x_config_times.csv
 prints the candidate table for gsr_api.hip and the fit's distance from the
@@ -38,13 +39,12 @@ CUS = 256
 Shape = Tuple[int, int, int]
 # the selector's candidates; the copy-wave K-split tiles only for K > 256,
 # their four-wave twins only for K <= 256
-BASE = [15, 23, 24, 5, 6, 7, 10, 8]
+BASE = [28, 23, 24, 5, 6, 7, 10, 8]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
 # (config, its 16x16x32 stand-in, the tile whose grid size decides)
-FULL_CHIP = [(15, 25, (256, 256)), (23, 26, (128, 256))]
+FULL_CHIP = [(23, 26, (128, 256))]
 ALL = BASE + [f for _, f, _ in FULL_CHIP] + COPY_WAVE + FOUR_WAVE
-FULL_GRID = (64, 96, 128, 160, 192, 224, 256, 320)
 FULL_H_GRID = (128, 160, 176, 192, 208, 224, 256, 320)
 NEVER = 1 << 30
 
@@ -150,17 +150,16 @@ def _search(times, tiles, a_grid, p_grid, fulls):
     return best
 
 
-def fit(times, tiles, a_grid=None, p_grid=None, full_grid=None, full_h_grid=None):
-    """(mean, worst, a, pmin, (full[0], full[1]), params) of the best point,
-    by coordinate search: (full[0], a, pmin) without config 26, then full[1],
-    then (a, pmin) again."""
+def fit(times, tiles, a_grid=None, p_grid=None, full_h_grid=None):
+    """(mean, worst, a, pmin, (full[0],), params) of the best point, by
+    coordinate search: (a, pmin) without config 26, then full[0], then
+    (a, pmin) again."""
     a_grid = np.arange(0.0, 0.75, 0.05) if a_grid is None else a_grid
-    p_grid = np.arange(0.30, 0.90, 0.05) if p_grid is None else p_grid
-    full_grid = FULL_GRID if full_grid is None else full_grid
+    p_grid = np.arange(0.30, 1.001, 0.05) if p_grid is None else p_grid
     full_h_grid = FULL_H_GRID if full_h_grid is None else full_h_grid
-    best = _search(times, tiles, a_grid, p_grid, [(int(f), NEVER) for f in full_grid])
-    f0, a, p = best[4][0], best[2], best[3]
-    best = _search(times, tiles, [a], [p], [(f0, int(f)) for f in full_h_grid])
+    best = _search(times, tiles, a_grid, p_grid, [(NEVER,)])
+    a, p = best[2], best[3]
+    best = _search(times, tiles, [a], [p], [(int(f),) for f in full_h_grid])
     return _search(times, tiles, a_grid, p_grid, [best[4]])
 
 
