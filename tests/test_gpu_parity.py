@@ -147,25 +147,28 @@ def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
         PT.assert_parity(f"{shape} cfg21", PT.run_gpu(a, b, 0.5, config_id=21), ref)
 
 
-# The 256x256 16x16x32 kernel with B copied to LDS (config 28) and its
-# register-transpose twin (config 25) pair the same k in every MFMA and sum in
-# the same order, so they give the same bits; K covers 1 to 65 steps of 64,
-# M and N ragged against the tile, the element path included (N or K odd).
+# The 16x16x32 kernels with B copied to LDS (config 28: 256x256, config 29:
+# 128x256) and their register-transpose twins (configs 25 and 26) pair the
+# same k in every MFMA and sum in the same order, so they give the same bits;
+# K covers 1 to 65 steps of 64, M and N ragged against the tile, the element
+# path included (N or K odd).
+@pytest.mark.parametrize("pair", [(28, 25), (29, 26)], ids=lambda p: f"{p[0]}vs{p[1]}")
 @pytest.mark.parametrize("shape", [(256, 256, 8), (300, 520, 200), (257, 1031, 72), (1000, 1500, 704),
                                    (513, 777, 4160), (4097, 2048, 1000), (2048, 4096, 1031)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_copy_transpose_twin_matches_register_transpose(gsr, orc, shape):
+def test_copy_transpose_twin_matches_register_transpose(gsr, orc, shape, pair):
     M, N, K = shape
+    new, old = pair
     a, b = W.normal_inputs(M, N, K, seed=M + 7 * N + 3 * K)
     ad, bd = a.to(DEV), b.to(DEV)
-    say(f"[gpu] config 28 vs 25 {shape}")
-    c28 = gsr.gemm_scale_relu_ex(ad, bd, 0.5, 28).clone()
-    c25 = gsr.gemm_scale_relu_ex(ad, bd, 0.5, 25).clone()
+    say(f"[gpu] config {new} vs {old} {shape}")
+    c_new = gsr.gemm_scale_relu_ex(ad, bd, 0.5, new).clone()
+    c_old = gsr.gemm_scale_relu_ex(ad, bd, 0.5, old).clone()
     torch.cuda.synchronize()
-    assert torch.equal(c28.view(torch.int16), c25.view(torch.int16)), shape
+    assert torch.equal(c_new.view(torch.int16), c_old.view(torch.int16)), shape
     if M * N * K <= 3e9:
         ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
-        PT.assert_parity(f"{shape} cfg28", bits(c28.cpu()), ref)
+        PT.assert_parity(f"{shape} cfg{new}", bits(c_new.cpu()), ref)
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 200), (257, 263, 129), (1024, 1024, 512),
@@ -218,7 +221,7 @@ def test_empty_outputs(gsr):
     assert gsr.gemm_scale_relu(a2, b2, 0.5).shape == (4, 0)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 17, 18, 21, 22, 23, 24, 25, 26, 28])
+@pytest.mark.parametrize("cid", [-1, 5, 17, 18, 21, 22, 23, 24, 25, 26, 28, 29])
 def test_c_aligned_to_8_not_16_bytes(gsr, orc, cid):
     """A and B 16-byte aligned, C only 8-byte aligned (4 elements into a 16-byte
     aligned buffer): the 128-bit stores need 16-byte aligned rows of C, so
@@ -258,7 +261,7 @@ def test_unaligned_pointers(gsr, orc, offset):
     PT.assert_parity(f"unaligned+{offset}", bits(cd.cpu()), ref)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 21, 23, 24, 25, 26, 28])
+@pytest.mark.parametrize("cid", [-1, 5, 21, 23, 24, 25, 26, 28, 29])
 def test_guard_bands_and_full_coverage(gsr, orc, cid):
     """C sits inside a larger buffer filled with a sentinel: the bands before
     and after stay untouched and every element of C is written."""

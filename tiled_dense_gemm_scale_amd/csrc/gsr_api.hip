@@ -64,9 +64,10 @@ hipError_t launch_ilv16(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), s, p);
 }
 
+template <class T>
 hipError_t launch_ilv16d(const Problem& p, int grid, hipStream_t s)
 {
-    return launch_kernel(gsr::gemm_scale_relu_ilv16d_kernel, dim3(grid), dim3(gsr::Ilv16DCfg::NT), s, p);
+    return launch_kernel(gsr::gemm_scale_relu_ilv16d_kernel<T>, dim3(grid), dim3(T::NT), s, p);
 }
 
 hipError_t launch_ilv16h(const Problem& p, int grid, hipStream_t s)
@@ -170,7 +171,9 @@ const Entry kTable[] = {
     GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h, 1),
     // configuration 25 with B copied to LDS as stored and read with transpose reads: the
     // selector's 256x256 tile
-    GSR_ILV(28, 256, 256, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d, 2),
+    GSR_ILV(28, 256, 256, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16DCfg>, 2),
+    // configuration 26 with B copied to LDS as stored and read with transpose reads
+    GSR_ILV(29, 128, 256, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 

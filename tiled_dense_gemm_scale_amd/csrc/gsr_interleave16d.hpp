@@ -1,20 +1,23 @@
-// gsr_interleave16d.hpp -- the 256x256 explicitly interleaved kernel on the
+// gsr_interleave16d.hpp -- the explicitly interleaved kernels on the
 // 16x16x32 fp16 MFMA with both operands copied global -> LDS by the buffer
-// unit.
+// unit: 256x256 tiles (configuration 28) and 128x256 tiles (configuration 29).
 //
-// Tile, waves, accumulators, A path, A^T fragments, launch order and
-// epilogue are those of gsr_interleave16.hpp.  What changes is B: instead of
+// Waves, accumulators, A path, A^T fragments, launch order and epilogue are
+// those of the register-transpose kernels in gsr_interleave16.hpp (256x256)
+// and gsr_interleave16h.hpp (128x256).  What changes is B: instead of
 // loading an 8x8 block per thread into registers, transposing it with byte
 // permutes and writing B^T rows to LDS, the buffer unit copies B straight
 // into LDS as it is stored (64 k-rows of 256 n, 512 bytes each), and each
 // B^T fragment is assembled from two gfx950 transpose reads
 // (ds_read_b64_tr_b16), each handing a lane four k-consecutive values of one
-// column.  Timing variants of the register-transpose kernel with single
-// parts of a K-step removed (same addresses, outputs not valid) put the B
-// register path -- 8 global loads, 32 permutes and 8 LDS writes per wave per
-// step -- at about a quarter of the kernel's time at 16384^3, more than the
-// A copies (8 %) or all operand reads (9 %); the copies and transpose reads
-// that replace it move the same bytes through LDS.
+// column.  Timing variants of the register-transpose 256x256 kernel with
+// single parts of a K-step removed (same addresses, outputs not valid) put
+// the B register path -- 8 global loads, 32 permutes and 8 LDS writes per
+// wave per step -- at about a quarter of the kernel's time at 16384^3, more
+// than the A copies (8 %) or all operand reads (9 %); the copies and
+// transpose reads that replace it move the same bytes through LDS.  Both
+// tiles keep B 256 wide, so every wave owns 128 columns and the B copy plan,
+// swizzle and reads are one code for both.
 //
 // B layout in a stage: row k (0..63) at k * 512, its 16-byte chunk c at
 // physical chunk c ^ fb(k), fb(k) = 2 * ((k mod 4) + 4 * s((k / 8) mod 4)),
@@ -24,25 +27,31 @@
 // eight rows that the LDS serves in one cycle (lane groups 0 and 1, or 0 and
 // 2, either way) then sit on eight distinct 32-byte bank slots.
 //
-// LDS: A0 | A1 | B0 | B1 | B2 (160 KiB).  Step t reads A stage t mod 2 and
-// B stage t mod 3; the loop is unrolled over six steps so every stage offset
-// is a constant.  A third B stage lets the copies of a step be spread over
-// both substeps of the step before the one that publishes them: timing
-// variants with all 16 copies of a step packed into one substep after the
-// barrier ran 5-6 % slower than with the same copies spread over that
-// substep, and with only A's or B's copies removed each set still cost about
-// 13 %, so the copies are given the whole K-step.
+// LDS: A0 | A1 | B0 | B1 | B2 (160 KiB at 256x256, 128 KiB at 128x256).
+// Step t reads A stage t mod 2 and B stage t mod 3; the loop is unrolled
+// over six steps so every stage offset is a constant.  A third B stage lets
+// the copies of a step be spread over both substeps of the step before the
+// one that publishes them: timing variants of the 256x256 kernel with all 16
+// copies of a step packed into one substep after the barrier ran 5-6 %
+// slower than with the same copies spread over that substep, and with only
+// A's or B's copies removed each set still cost about 13 %, so the copies
+// are given the whole K-step.
 //
-// Companions of step t (A stage SA = t mod 2, B stage SB = t mod 3):
+// A K-step is two 32-deep substeps of FM x FN MFMAs (FN = 8 B^T fragments
+// of 16 columns, FM = 8 or 4 A^T fragments of 16 rows); slot i of a substep
+// multiplies X[i / FM] with Y[i % FM].  Companions of step t (A stage
+// SA = t mod 2, B stage SB = t mod 3), slots for 256x256 / 128x256:
 //   substep 0: reads of substep 1's operands (X[a] as two transpose reads at
-//              slots 8a + 8 and 8a + 9, X[7] at 44 and 45, Y[b] every fourth
-//              slot from 2); the copies of B(t+2) into B stage (t+2) mod 3,
-//              freed at step t-1's barrier, every eighth slot from 4;
-//   substep 1, slot 6: wait for the A(t+1) and B(t+1) copies, barrier
+//              slots FM (a + 1) and FM (a + 1) + 1, X[7] at 44, 45 / 18, 19,
+//              Y[b] every fourth slot from 2); the eight copies of B(t+2)
+//              into B stage (t+2) mod 3, freed at step t-1's barrier, every
+//              eighth slot from 4 / every fourth slot from 3;
+//   substep 1, slot 6 / 4: wait for the A(t+1) and B(t+1) copies, barrier
 //              (publishes step t+1, frees A stage SA); then the copies of
-//              A(t+2) into A stage SA every seventh slot from 8, and the
-//              reads of step t+1's substep-0 operands (X[7] at 60 and 61,
-//              Y[b] every fourth slot from 10).
+//              A(t+2) into A stage SA (8 every seventh slot from 8 / 4 every
+//              fourth slot from 5), and the reads of step t+1's substep-0
+//              operands (X[a] as in substep 0, X[7] at 60, 61 / 26, 27, Y[b]
+//              every fourth slot from 10 / 6).
 #pragma once
 
 #include <type_traits>
@@ -51,17 +60,42 @@
 
 namespace gsr {
 
+// The 256x256 tile (configuration 28) and its slot plan.
 struct Ilv16DCfg : Ilv16Cfg {
     static constexpr int ROWB = BN * 2;                 // 512-byte B rows
     static constexpr int B_PER = B_BYTES / 1024 / NW;   // 8 copies per wave per step
     static constexpr int B_STAGES = 3;
     static constexpr int LDS_BYTES = 2 * A_BYTES + B_STAGES * B_BYTES;  // 160 KiB
-    static_assert(B_PER == 8 && A_PER == 8, "the unit plan places 8 + 8 copies");
-    static_assert(BK == 64 && BN == 256, "the B swizzle and read plan assume 64 rows of 32 chunks");
-    static_assert(LDS_BYTES <= 163840, "LDS budget of one workgroup on gfx950");
-    // ds_read offsets are 16 bits: B stages 0 and 1, substep and read ride in
-    // them (stage 2 has a base register of its own)
-    static_assert(B_BYTES + 32 * ROWB + 4 * ROWB < 65536, "B read offsets fit the immediate field");
+    static constexpr int SLOTS = FM * FN;               // 64 MFMAs per substep
+    static constexpr int X7_0 = 44, X7_1 = 60;          // X[7] reads in substeps 0 and 1
+    static constexpr int Y0_0 = 2, Y0_1 = 10;           // first Y read in substeps 0 and 1
+    static constexpr int BAR = 6;                       // wait + barrier slot of substep 1
+    static constexpr int BC0 = 4, BCD = 8;              // B copies in substep 0: first slot, stride
+    static constexpr int AC0 = 8, ACD = 7;              // A copies in substep 1: first slot, stride
+};
+
+// The 128x256 tile (configuration 29): four waves of 64x128, 8 (n) x 4 (m)
+// blocks of 16x16 per wave, 32 MFMAs per substep; A stages of 16 KiB, B
+// stages as above (2 x 16 + 3 x 32 = 128 KiB).
+struct Ilv16HDCfg {
+    static constexpr int BM = 128, BN = 256, BK = 64, WM = 2, WN = 2;
+    static constexpr int NW = WM * WN, NT = kWave * NW;
+    static constexpr int CH = BK / 8;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;  // 4 (m) x 8 (n) blocks of 16x16
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int B_REGION = 2 * A_BYTES;
+    static constexpr int ROWB = BN * 2;
+    static constexpr int A_PER = A_BYTES / 1024 / NW;   // 4 copies per wave per step
+    static constexpr int B_PER = B_BYTES / 1024 / NW;   // 8
+    static constexpr int B_STAGES = 3;
+    static constexpr int LDS_BYTES = 2 * A_BYTES + B_STAGES * B_BYTES;  // 128 KiB
+    static constexpr int SLOTS = FM * FN;               // 32 MFMAs per substep
+    static constexpr int X7_0 = 18, X7_1 = 26;
+    static constexpr int Y0_0 = 2, Y0_1 = 6;
+    static constexpr int BAR = 4;
+    static constexpr int BC0 = 3, BCD = 4;
+    static constexpr int AC0 = 5, ACD = 4;
 };
 
 // Physical-chunk mask of B row k (bits 1..3 of the chunk index only).
@@ -71,11 +105,25 @@ __device__ __forceinline__ uint32_t fb16(uint32_t k)
     return ((k & 3u) + (((c ^ (c >> 1)) & 1u) << 2)) << 1;
 }
 
+template <class T>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_scale_relu_ilv16d_kernel(Problem p)
 {
-    using T = Ilv16DCfg;
     constexpr int BK = T::BK, CH = T::CH, FM = T::FM, FN = T::FN;
+    static_assert(BK == 64 && T::BN == 256 && T::WTN == 128, "the B swizzle and read plan assume 64 rows of 32 chunks");
+    static_assert(T::LDS_BYTES <= 163840, "LDS budget of one workgroup on gfx950");
+    // ds_read offsets are 16 bits: B stages 0 and 1, substep and read ride in
+    // them (stage 2 has a base register of its own)
+    static_assert(T::B_BYTES + 32 * T::ROWB + 4 * T::ROWB < 65536, "B read offsets fit the immediate field");
+    // the slot plan: every copy inside its substep, the barrier before any
+    // read of the stages it publishes, X[7] and the Y reads in free registers
+    // and early enough for their first MFMA
+    static_assert(T::SLOTS == FM * FN && T::B_PER == 8 && FN == 8, "eight B^T fragments, eight B copies");
+    static_assert(T::BC0 + T::BCD * (T::B_PER - 1) < T::SLOTS, "B copies fit substep 0");
+    static_assert(T::AC0 > T::BAR && T::AC0 + T::ACD * (T::A_PER - 1) < T::SLOTS, "A copies follow the barrier");
+    static_assert(T::Y0_1 >= T::BAR && T::X7_1 >= T::BAR && FM >= T::BAR, "reads of the new stages follow the barrier");
+    static_assert(T::X7_0 + 1 < FM * (FN - 1) && T::Y0_0 + 4 * (FM - 1) < T::SLOTS && T::Y0_1 + 4 * (FM - 1) < T::SLOTS,
+                  "operands of the next substep are read within this one");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];  // A0 | A1 | B0 | B1 | B2
 
@@ -202,17 +250,18 @@ gemm_scale_relu_ilv16d_kernel(Problem p)
         dst = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::A_BYTES + (b >> 2) * (64 * BK * 2) + yb[ks][b & 3]));
     };
     // The reads of slot i of a substep, all for the next substep (A stage SR,
-    // B stage BR, substep kr): X[a] (a < 7) at slots 8a + 8 and 8a + 9, as
-    // soon as its last MFMA here has issued; X[7] (into the other X7
-    // register) at x7 and x7 + 1; Y[b] at slot y0 + 4b.
+    // B stage BR, substep kr): X[a] (a < 7) at slots FM (a + 1) and
+    // FM (a + 1) + 1, as soon as its last MFMA here has issued; X[7] (into
+    // the other X7 register) at x7 and x7 + 1; Y[b] at slot y0 + 4b.
     auto reads = [&](int i, int SR, int BR, int kr, half8 (&ynext)[FM], int y0, int x7) {
-        if (i >= 8 && i <= 8 * (FN - 1) + 1 && (i & 7) < 2) read_xh(BR, kr, (i >> 3) - 1, i & 1);
+        if (i >= FM && i <= FM * (FN - 1) + 1 && (i % FM) < 2) read_xh(BR, kr, i / FM - 1, i % FM);
         if (i == x7 || i == x7 + 1) read_xh(BR, kr, FN - 1, i - x7);
         if (i >= y0 && i < y0 + 4 * FM && ((i - y0) & 3) == 0) read_y(SR, kr, (i - y0) >> 2, ynext[(i - y0) >> 2]);
     };
+    // slot i multiplies B^T fragment X[i / FM] with A^T fragment Y[i % FM]
     auto mma = [&](int i, int ks, const half8 (&ys)[FM]) {
-        const int a = i >> 3;
-        mfma16_inplace(acc[a][i & 7], a == FN - 1 ? X7[ks] : X[a], ys[i & 7]);
+        const int a = i / FM;
+        mfma16_inplace(acc[a][i % FM], a == FN - 1 ? X7[ks] : X[a], ys[i % FM]);
     };
 
     // One K-step: A stage SA = t mod 2, B stage SB = t mod 3.
@@ -227,10 +276,10 @@ gemm_scale_relu_ilv16d_kernel(Problem p)
         {
             const i32x4 rb = b_rsrc(k2);
 #pragma unroll
-            for (int i = 0; i < 64; ++i) {
+            for (int i = 0; i < T::SLOTS; ++i) {
                 mma(i, 0, Y[0]);
-                reads(i, SA, SB, 1, Y[1], 2, 44);
-                if (i >= 4 && (i & 7) == 4) copy_b(SB2, (i - 4) >> 3, rb);
+                reads(i, SA, SB, 1, Y[1], T::Y0_0, T::X7_0);
+                if (i >= T::BC0 && (i - T::BC0) % T::BCD == 0) copy_b(SB2, (i - T::BC0) / T::BCD, rb);
                 sched_fence();
             }
         }
@@ -240,14 +289,15 @@ gemm_scale_relu_ilv16d_kernel(Problem p)
             const uint32_t kleft2 = (k2 < K) ? K - k2 : 0u;
             const i32x4 ra = a_rsrc(k2);
 #pragma unroll
-            for (int i = 0; i < 64; ++i) {
+            for (int i = 0; i < T::SLOTS; ++i) {
                 mma(i, 1, Y[1]);
-                if (i == 6) {
+                if (i == T::BAR) {
                     wait_vmcnt<T::B_PER>();  // A(t+1), B(t+1) are in; B(t+2) may not be
                     lds_barrier();
                 }
-                if (i > 6) reads(i, SAN, SBN, 0, Y[0], 10, 60);
-                if (i >= 8 && i <= 57 && (i - 8) % 7 == 0) copy_a(SA, (i - 8) / 7, kleft2, ra);
+                if (i >= T::BAR) reads(i, SAN, SBN, 0, Y[0], T::Y0_1, T::X7_1);
+                if (i >= T::AC0 && (i - T::AC0) % T::ACD == 0 && (i - T::AC0) / T::ACD < T::A_PER)
+                    copy_a(SA, (i - T::AC0) / T::ACD, kleft2, ra);
                 sched_fence();
             }
         }
