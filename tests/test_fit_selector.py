@@ -14,37 +14,34 @@ API = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc", "gsr_api.hip")
 
 def test_fit_recovers_a_known_model():
     """Times generated from known rates and fixed costs are fitted back."""
-    tiles = {28: (256, 256), 23: (128, 256), 24: (128, 128), 5: (256, 128), 6: (128, 256), 7: (128, 128), 10: (64, 128),
-             8: (128, 64), 26: (128, 256), 21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
+    tiles = {28: (256, 256), 29: (128, 256), 24: (128, 128), 5: (256, 128), 10: (64, 128), 8: (128, 64),
+             21: (64, 64), 22: (32, 64), 16: (64, 64), 18: (32, 64)}
     truth = {cid: (1.0 + 0.5 * i, 2.0 + 0.25 * i) for i, cid in enumerate(sorted(tiles))}
-    a, pmin, full = 0.2, 0.6, (160,)
+    a, pmin = 0.2, 0.6
     times = {}
     for M in (16, 200, 1000, 4100, 8200):
         for N in (512, 3000, 11008):
             for K in (128, 256, 1024, 4096):
                 times[(M, N, K)] = {cid: F.waves(F.workgroups(tiles[cid], M, N), a, pmin)
                                     * (2.0 * tiles[cid][0] * tiles[cid][1] * K / (r * 1e6) + e)
-                                    for cid, (r, e) in truth.items() if cid in F.candidates(M, N, K, full)}
-    params = F.fit_params(times, tiles, a, pmin, full)
+                                    for cid, (r, e) in truth.items() if cid in F.candidates(M, N, K)}
+    params = F.fit_params(times, tiles, a, pmin)
     for cid, (r, e) in truth.items():
         assert params[cid][0] == pytest.approx(r, rel=1e-6)
         assert params[cid][1] == pytest.approx(e, rel=1e-6, abs=1e-9)
-    mean, worst = F.regret(times, tiles, params, a, pmin, full)
+    mean, worst = F.regret(times, tiles, params, a, pmin)
     assert mean == pytest.approx(1.0) and worst == pytest.approx(1.0)
 
 
-def test_full_chip_rule_swaps_the_128x256_tile_kernels():
-    f = (176,)
-    # one 256x256 kernel at every grid size
-    for M, N in ((1024, 4096), (4096, 4096), (16, 11008), (2304, 4096)):
-        assert 28 in F.candidates(M, N, 4096, f) and 15 not in F.candidates(M, N, 4096, f)
-        assert 25 not in F.candidates(M, N, 4096, f)
-    # the 128x256 pair: 2048 x 4096 is 16 x 16 = 256 tiles, 1408 x 4096 is 11 x 16 = 176, 1280 x 4096 160
-    assert 26 in F.candidates(2048, 4096, 4096, f) and 23 not in F.candidates(2048, 4096, 4096, f)
-    assert 26 in F.candidates(1408, 4096, 4096, f) and 23 not in F.candidates(1408, 4096, 4096, f)
-    assert 23 in F.candidates(1280, 4096, 4096, f) and 26 not in F.candidates(1280, 4096, 4096, f)
-    assert 23 in F.candidates(2048, 4096, 4096, (F.NEVER,))
-    assert F.candidates(16, 11008, 256, f)[-2:] == F.FOUR_WAVE and F.candidates(16, 11008, 257, f)[-2:] == F.COPY_WAVE
+def test_one_kernel_per_large_tile():
+    """One 256x256 and one 128x256 kernel at every grid size (the copy-to-LDS
+    16x16x32 kernels; their register-transpose twins and the 32x32x16 128x256
+    kernel are never candidates), and the K-split kinds by K."""
+    for M, N in ((16, 11008), (1024, 4096), (1280, 4096), (2048, 4096), (4096, 4096)):
+        c = F.candidates(M, N, 4096)
+        assert 28 in c and 29 in c
+        assert not {6, 7, 15, 23, 25, 26} & set(c)
+    assert F.candidates(16, 11008, 256)[-2:] == F.FOUR_WAVE and F.candidates(16, 11008, 257)[-2:] == F.COPY_WAVE
 
 
 def test_waves_price_a_partial_last_wave():
@@ -59,7 +56,7 @@ def test_selector_table_is_the_fit_of_the_committed_measurements():
     """The constants in select() are what the fit of the committed times gives."""
     times, tiles = F.load(CSV)
     assert len(times) >= 50
-    mean, worst, a, pmin, full, params = F.fit(times, tiles)
+    mean, worst, a, pmin, params = F.fit(times, tiles)
     src = open(API).read()
     table = src[src.index("const Candidate kCandidates[]"):]
     table = table[: table.index("};")]
@@ -71,8 +68,7 @@ def test_selector_table_is_the_fit_of_the_committed_measurements():
         assert tile_us == pytest.approx(params[cid][1], abs=0.006), cid
     consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
     assert float(consts.group(1)) == pytest.approx(pmin) and float(consts.group(2)) == pytest.approx(a)
-    assert re.search(r"kFullChipTiles = ", src) is None  # one 256x256 kernel, no rule
-    assert int(re.search(r"kFullChipTilesH = (\d+);", src).group(1)) == full[0]
+    assert re.search(r"kFullChipTiles", src) is None  # one kernel per large tile, no swap rule
     assert mean < 1.005 and worst < 1.05
 
 
@@ -81,12 +77,11 @@ def test_library_selector_matches_the_model(native):
     times, tiles = F.load(CSV)
     src = open(API).read()
     consts = re.search(r"kPartMin = ([0-9.]+), kPartA = ([0-9.]+);", src)
-    full_h = int(re.search(r"kFullChipTilesH = (\d+);", src).group(1))
-    mean, worst, a, pmin, full, params = F.fit(times, tiles, a_grid=np.array([float(consts.group(2))]),
-                                               p_grid=np.array([float(consts.group(1))]), full_h_grid=(full_h,))
+    mean, worst, a, pmin, params = F.fit(times, tiles, a_grid=np.array([float(consts.group(2))]),
+                                         p_grid=np.array([float(consts.group(1))]))
     disagree = []
     for (M, N, K), t in times.items():
-        want = F.choose(params, tiles, M, N, K, a, pmin, full)
+        want = F.choose(params, tiles, M, N, K, a, pmin)
         got = native.select_config(M, N, K)["id"]
         if got != want:
             disagree.append(((M, N, K), got, want))

@@ -48,7 +48,7 @@ def test_largest_operand_under_2gib(gsr, orc, K):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cid", [23, 25, 26, 28, 29])
+@pytest.mark.parametrize("cid", [25, 26, 28, 29])
 def test_largest_operand_under_2gib_interleaved(gsr, orc, cid):
     """The same A just under 2^31 bytes through each interleaved 256x256 and
     128x256 kernel, forced: their per-lane copy offsets are formed from base
@@ -88,7 +88,7 @@ def test_concurrent_host_threads(gsr, tmp_path):
         want.append(gsr.gemm_scale_bias_act(a, b, bias if i % 2 else None, 0.5, acts[i % 3]).clone())
     torch.cuda.synchronize()
     table = tmp_path / "t.txt"
-    table.write_text("".join(f"{M} {N} {K} 7 2 0\n" for (M, N, K) in shapes[:2]))
+    table.write_text("".join(f"{M} {N} {K} 8 2 0\n" for (M, N, K) in shapes[:2]))
     errors = []
     stop = threading.Event()
 

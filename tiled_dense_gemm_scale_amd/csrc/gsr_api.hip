@@ -17,7 +17,6 @@
 #include "gsr_interleave.hpp"
 #include "gsr_ksplit.hpp"
 #include "gsr_kspec.hpp"
-#include "gsr_interleave_h.hpp"
 #include "gsr_interleave_q.hpp"
 #include "gsr_interleave16.hpp"
 #include "gsr_interleave16h.hpp"
@@ -75,10 +74,6 @@ hipError_t launch_ilv16h(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilv16h_kernel, dim3(grid), dim3(gsr::Ilv16HCfg::NT), s, p);
 }
 
-hipError_t launch_ilvh(const Problem& p, int grid, hipStream_t s)
-{
-    return launch_kernel(gsr::gemm_scale_relu_ilvh_kernel, dim3(grid), dim3(256), s, p);
-}
 
 hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
 {
@@ -142,15 +137,14 @@ struct Entry {
 
 // The compiled tile table, by id.  Ids are stable from one library version to
 // the next, so a tuning table written earlier keeps its meaning; the ids of
-// configurations that were dropped (0-4, 9, 11-15, 19, 20: tiles that neither
-// the selector nor any measured tuning entry chose; 15, the 256x256 tile on
-// 32x32x16 MFMAs, was slower than configuration 28 on every measured shape)
-// are not reused and are rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is made
-// by select().
+// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23: tiles
+// that neither the selector nor any measured tuning entry chose; 15 and 23,
+// the 256x256 and 128x256 tiles on 32x32x16 MFMAs, were slower than
+// configurations 28 and 29 on every measured shape) are not reused and are
+// rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is
+// made by select().
 const Entry kTable[] = {
     GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
-    GSR_PIPE(6, 128, 256, 64, 2, 2, 3, 4),   // 4 waves of 64x128
-    GSR_PIPE(7, 128, 128, 64, 2, 2, 4, 4),   // 4 waves of 64x64, 4 x 32 KiB
     GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
     GSR_PIPE(10, 64, 128, 64, 2, 2, 6, 4),   // 4 waves of 32x64
     GSR_KSPLIT(16, 64, 64, 4, 4),            // 4 waves split K, whole 64x64 tile each
@@ -159,20 +153,20 @@ const Entry kTable[] = {
     // K split with separate copy waves (eight waves per workgroup), two steps ahead
     GSR_KSPEC(21, 64, 64, 4, 2, 4),
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
-    // explicit interleave at half height, 4 waves of 64x128
-    GSR_ILV(23, 128, 256, gsr::IlvHCfg::LDS_BYTES, launch_ilvh, 1),
     // explicit interleave at a quarter of 256x256, 4 waves of 64x64
     GSR_ILV(24, 128, 128, gsr::IlvQCfg::LDS_BYTES, launch_ilvq, 1),
     // 256x256 on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave), B transposed through
     // registers: configuration 28's twin (same bits), kept for comparison; chip rounds of
     // 16 x 16 tiles where the grid divides into them
     GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16, 2),
-    // config 23's tile and data flow on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave)
+    // 128x256 on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave), B transposed through
+    // registers: configuration 29's twin (same bits), kept for comparison
     GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h, 1),
     // configuration 25 with B copied to LDS as stored and read with transpose reads: the
     // selector's 256x256 tile
     GSR_ILV(28, 256, 256, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16DCfg>, 2),
-    // configuration 26 with B copied to LDS as stored and read with transpose reads
+    // configuration 26 with B copied to LDS as stored and read with transpose reads: the
+    // selector's 128x256 tile
     GSR_ILV(29, 128, 256, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
@@ -190,58 +184,49 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.90, fill) of a full one (a part-filled chip runs at a
-// higher power-limited clock, but every tile still pays its fixed cost).  The
-// 256x256 tile is configuration 28 (16x16x32 MFMAs, B copied to LDS), faster
-// than the other 256x256 kernels on every measured shape; the 128x256 tile
-// has two kernels: config 23 (32x32x16 MFMAs, the higher issue efficiency)
-// and config 26 (16x16x32, the higher engine clock on random data once the
-// power limit binds), which takes config 23's place from 160 workgroups of
-// 128x256.  The rates, overheads, the partial-wave form and the threshold were
-// fitted (least squares in relative error for the rates, then the grid point
-// whose choices come closest to the fastest configuration) to the times of
-// every configuration on 60 shapes measured on one MI355X (M from 1 to 8192
-// against 11008x4096, 4096x4096 and 4096x11008 weights, squares from 256 to
-// 16384, and the benchmark workloads), the offline sweep the aikraft.ru
-// guide describes in sections 3 and 7 (tiled_dense_gemm_scale_amd/
-// fit_selector.py on tuning/mi355x_config_times.csv reproduces this table);
-// on those shapes the choice is on average within 0.05 % of the fastest
-// configuration.  Below K = 256 the four-wave K-split tiles replace their
-// copy-wave twins (at two K-steps the copy waves have nothing to run ahead
-// of).
+// full costs max(0.70, 0.60 + 0.40 * fill) of a full one (a part-filled chip
+// runs at a higher power-limited clock, but every tile still pays its fixed
+// cost).  The 256x256 and 128x256 tiles have one candidate each, the
+// 16x16x32 kernels with B copied to LDS (configurations 28 and 29): each was
+// faster than every other kernel of its tile on every measured shape.  The
+// rates, overheads and the partial-wave form were fitted (least squares in
+// relative error for the rates, then the grid point whose choices come
+// closest to the fastest configuration) to the times of every configuration
+// on 60 shapes measured on one MI355X (M from 1 to 8192 against 11008x4096,
+// 4096x4096 and 4096x11008 weights, squares from 256 to 16384, and the
+// benchmark workloads), the offline sweep the aikraft.ru guide describes in
+// sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
+// tuning/mi355x_config_times.csv reproduces this table); on those shapes the
+// choice is on average within 0.1 % of the fastest configuration, 2.1 % at
+// worst.  Below K = 256 the four-wave K-split tiles replace their copy-wave
+// twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
     int id;
     double tflops_per_cu;  // rate of one CU on this tile while the chip is busy
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {28, 6.97, 7.33},   // 256x256, 16x16x32, B copied to LDS
-    {23, 5.28, 6.12},   // 128x256, explicit interleave, 32x32x16 (grids below 160 tiles)
-    {24, 3.43, 3.78},   // 128x128, explicit interleave
-    {5, 4.08, 6.54},    // 256x128
-    {6, 3.91, 6.48},    // 128x256
-    {7, 3.26, 4.53},    // 128x128
-    {10, 1.99, 3.81},   // 64x128
-    {8, 2.30, 3.75},    // 128x64
-    {26, 4.15, 0.18},   // 128x256, explicit interleave, 16x16x32 (grids of 160 tiles or more)
-    {21, 2.70, 3.03},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.78, 2.31},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.41, 3.43},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.62, 2.75},   // 32x64, K split, four waves       (K <= 256)
+    {28, 6.086, 10.619},  // 256x256, 16x16x32, B copied to LDS
+    {29, 5.444, 7.450},   // 128x256, 16x16x32, B copied to LDS
+    {24, 3.341, 5.804},   // 128x128, explicit interleave
+    {5, 3.807, 9.881},    // 256x128
+    {10, 1.971, 5.517},   // 64x128
+    {8, 2.345, 5.344},    // 128x64
+    {21, 2.785, 3.523},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.822, 2.592},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.512, 4.101},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.656, 3.130},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.90, kPartA = 0.00;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
-constexpr int64_t kFullChipTilesH = 160;          // config 26 instead of config 23 from this many 128x256 tiles
+constexpr double kPartMin = 0.70, kPartA = 0.60;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 
 int select(int64_t M, int64_t N, int64_t K)
 {
     const double cus = 256.0;
-    const bool full_chip_h = cdiv(M, 128) * cdiv(N, 256) >= kFullChipTilesH;
     int best = 28;
     double best_t = 1e300;
     for (const Candidate& c : kCandidates) {
         const bool copy_wave = c.id == 21 || c.id == 22, four_wave = c.id == 16 || c.id == 18;
         if ((copy_wave && K <= 256) || (four_wave && K > 256)) continue;
-        if ((c.id == 23 && full_chip_h) || (c.id == 26 && !full_chip_h)) continue;
         const gsr_config& g = entry_of(c.id)->cfg;
         const double wgs = (double)cdiv(M, g.block_m) * (double)cdiv(N, g.block_n);
         const double full = std::floor(wgs / cus), fill = (wgs - full * cus) / cus;
@@ -355,7 +340,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 600; }
+int gsr_version(void) { return 700; }
 
 const char* gsr_status_string(int status)
 {

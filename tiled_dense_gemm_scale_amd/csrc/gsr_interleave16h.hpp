@@ -1,14 +1,12 @@
 // gsr_interleave16h.hpp -- the 128x256 explicitly interleaved kernel on the
-// 16x16x32 fp16 MFMA, for mid-size shapes whose 128x256 grid fills the chip
-// (e.g. 2048 x 4096 x 4096: 256 tiles).
+// 16x16x32 fp16 MFMA with B transposed through registers: the twin of the
+// 128x256 kernel in gsr_interleave16d.hpp (B copied to LDS), which gives the
+// same bits faster; kept for comparison.
 //
-// The tile, LDS stages and global traffic of the 128x256 kernel in
-// gsr_interleave_h.hpp (four waves of 64x128, A copied straight into LDS, B
-// one 8x8 block per thread through registers, both operands two K-steps
-// ahead, one barrier per K-step), with the matrix instruction, operand
-// fragments, register sets and LDS chunk order of the 256x256 16x16x32
-// kernel in gsr_interleave16.hpp, for the same reason: on random data the part
-// is power-limited and 16x16x32 MFMAs hold a higher engine clock.
+// Four waves of 64x128, A copied straight into LDS, B one 8x8 block per
+// thread through registers, both operands two K-steps ahead, one barrier per
+// K-step, with the matrix instruction, operand fragments, register sets and
+// LDS chunk order of the 256x256 16x16x32 kernel in gsr_interleave16.hpp.
 //
 // Each wave owns 64x128 of the tile as 8 (n) x 4 (m) accumulator blocks of
 // 16x16 (128 fp32 per lane, in AGPRs).  A K-step is two 32-deep substeps of

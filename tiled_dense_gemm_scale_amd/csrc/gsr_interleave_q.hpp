@@ -3,8 +3,7 @@
 // 128x128 tiles (e.g. 1024 x 4096 x 4096: 256 tiles of 128x128, 128 of
 // 128x256, 64 of 256x256).
 //
-// The interleave design of gsr_interleave.hpp (and of the 128x256 kernel in
-// gsr_interleave_h.hpp) on a 128x128 tile: four waves, each
+// The interleave design of gsr_interleave.hpp on a 128x128 tile: four waves, each
 // owning 64x64 of the tile (2 x 2 accumulator blocks), two LDS stages (A and B
 // 16 KiB each), A copied straight into LDS (4 copies per wave per step), every
 // operand read 128 bits wide, both operands requested two K-steps ahead, one

@@ -6,18 +6,14 @@ The selector in csrc/gsr_api.hip prices a candidate tile bm x bn as
 
 with wgs = ceil(M / bm) * ceil(N / bn) workgroups on 256 CUs and
 waves(wgs) = full waves + (a part-filled last wave: max(pmin, a + (1 - a) * fill)).
-The 256x256 tile has one kernel (config 28, 16x16x32 MFMAs with B copied to
-LDS: measured faster than both other 256x256 kernels on every one of the 60
-shapes).  The 128x256 tile has two: config 23 on 32x32x16 MFMAs (the higher
-issue efficiency) and config 26 on 16x16x32 MFMAs (the higher engine clock
-once enough CUs run for the power limit to bind); config 26 stands in for
-config 23 when the 128x256 grid has at least full[0] workgroups.  This module
-fits `rate` (TFLOP/s per CU) and `tile_us` per configuration by least squares
-in relative error on the shapes where it is a candidate, and picks (a, pmin,
-full) on grids whose choices come closest to the fastest measured
-configuration (mean log ratio): first (a, pmin) with config 26 left out, then
-full[0], then (a, pmin) again.  Input: the CSV written from a `tune.py --top 0`
-report (tuning/mi355x_config_times.csv) or such a JSON report itself.
+The 256x256 and 128x256 tiles have one kernel each, the 16x16x32 kernels with
+B copied to LDS (configs 28 and 29): each was measured faster than every other
+kernel of its tile on every one of the 60 shapes.  This module fits `rate`
+(TFLOP/s per CU) and `tile_us` per configuration by least squares in relative
+error, and picks (a, pmin) on a grid whose choices come closest to the
+fastest measured configuration (mean log ratio).  Input: the CSV written from
+a `tune.py --top 0` report (tuning/mi355x_config_times.csv) or such a JSON
+report itself.
 
     python -m tiled_dense_gemm_scale_amd.fit_selector tuning/mi355x_config_times.csv
 prints the candidate table for gsr_api.hip and the fit's distance from the
@@ -39,22 +35,14 @@ CUS = 256
 Shape = Tuple[int, int, int]
 # the selector's candidates; the copy-wave K-split tiles only for K > 256,
 # their four-wave twins only for K <= 256
-BASE = [28, 23, 24, 5, 6, 7, 10, 8]
+BASE = [28, 29, 24, 5, 10, 8]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
-# (config, its 16x16x32 stand-in, the tile whose grid size decides)
-FULL_CHIP = [(23, 26, (128, 256))]
-ALL = BASE + [f for _, f, _ in FULL_CHIP] + COPY_WAVE + FOUR_WAVE
-FULL_H_GRID = (128, 160, 176, 192, 208, 224, 256, 320)
-NEVER = 1 << 30
+ALL = BASE + COPY_WAVE + FOUR_WAVE
 
 
-def candidates(M: int, N: int, K: int, full) -> List[int]:
-    base = list(BASE)
-    for (cid, stand_in, tile), f in zip(FULL_CHIP, full):
-        if workgroups(tile, M, N) >= f:
-            base[base.index(cid)] = stand_in
-    return base + (COPY_WAVE if K > 256 else FOUR_WAVE)
+def candidates(M: int, N: int, K: int) -> List[int]:
+    return BASE + (COPY_WAVE if K > 256 else FOUR_WAVE)
 
 
 def load(path: str) -> Tuple[Dict[Shape, Dict[int, float]], Dict[int, Tuple[int, int]]]:
@@ -89,20 +77,14 @@ def workgroups(tile: Tuple[int, int], M: int, N: int) -> int:
     return -(-M // tile[0]) * -(-N // tile[1])
 
 
-PAIRED = {c for c, _, _ in FULL_CHIP} | {f for _, f, _ in FULL_CHIP}
-
-
-def fit_params(times, tiles, a: float, pmin: float, full) -> Dict[int, Tuple[float, float]]:
+def fit_params(times, tiles, a: float, pmin: float) -> Dict[int, Tuple[float, float]]:
     """(rate, tile_us) per candidate: least squares of t ~ w * (flops/rate + e),
-    rows scaled by 1/t (relative error); the paired configurations on the
-    shapes where the full-chip rules make them candidates."""
+    rows scaled by 1/t (relative error)."""
     out = {}
     for cid in ALL:
         X, y = [], []
         for (M, N, K), t in times.items():
             if cid not in t:
-                continue
-            if cid in PAIRED and cid not in candidates(M, N, K, full):
                 continue
             w = waves(workgroups(tiles[cid], M, N), a, pmin)
             X.append([w * 2.0 * tiles[cid][0] * tiles[cid][1] * K / 1e6, w])
@@ -115,9 +97,9 @@ def fit_params(times, tiles, a: float, pmin: float, full) -> Dict[int, Tuple[flo
     return out
 
 
-def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, full, have=None) -> int:
+def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, have=None) -> int:
     best, best_t = None, math.inf
-    for cid in candidates(M, N, K, full):
+    for cid in candidates(M, N, K):
         if cid not in params or (have is not None and cid not in have):
             continue
         rate, e = params[cid]
@@ -127,40 +109,30 @@ def choose(params, tiles, M: int, N: int, K: int, a: float, pmin: float, full, h
     return best
 
 
-def regret(times, tiles, params, a, pmin, full) -> Tuple[float, float]:
+def regret(times, tiles, params, a, pmin) -> Tuple[float, float]:
     """(mean, worst) of t[choice] / t[fastest] over the shapes."""
     logs, worst = [], 1.0
     for (M, N, K), t in times.items():
-        c = choose(params, tiles, M, N, K, a, pmin, full, have=t)
+        c = choose(params, tiles, M, N, K, a, pmin, have=t)
         r = t[c] / min(t.values())
         logs.append(math.log(r))
         worst = max(worst, r)
     return math.exp(sum(logs) / len(logs)), worst
 
 
-def _search(times, tiles, a_grid, p_grid, fulls):
-    best = None
-    for full in fulls:
-        for a in a_grid:
-            for p in p_grid:
-                params = fit_params(times, tiles, float(a), float(p), full)
-                mean, worst = regret(times, tiles, params, float(a), float(p), full)
-                if best is None or mean < best[0] - 1e-12:
-                    best = (mean, worst, float(a), float(p), full, params)
-    return best
-
-
-def fit(times, tiles, a_grid=None, p_grid=None, full_h_grid=None):
-    """(mean, worst, a, pmin, (full[0],), params) of the best point, by
-    coordinate search: (a, pmin) without config 26, then full[0], then
-    (a, pmin) again."""
+def fit(times, tiles, a_grid=None, p_grid=None):
+    """(mean, worst, a, pmin, params) of the grid point whose choices come
+    closest to the fastest configuration (first such point on ties)."""
     a_grid = np.arange(0.0, 0.75, 0.05) if a_grid is None else a_grid
     p_grid = np.arange(0.30, 1.001, 0.05) if p_grid is None else p_grid
-    full_h_grid = FULL_H_GRID if full_h_grid is None else full_h_grid
-    best = _search(times, tiles, a_grid, p_grid, [(NEVER,)])
-    a, p = best[2], best[3]
-    best = _search(times, tiles, [a], [p], [(int(f),) for f in full_h_grid])
-    return _search(times, tiles, a_grid, p_grid, [best[4]])
+    best = None
+    for a in a_grid:
+        for p in p_grid:
+            params = fit_params(times, tiles, float(a), float(p))
+            mean, worst = regret(times, tiles, params, float(a), float(p))
+            if best is None or mean < best[0] - 1e-12:
+                best = (mean, worst, float(a), float(p), params)
+    return best
 
 
 def main(argv=None) -> int:
@@ -169,13 +141,12 @@ def main(argv=None) -> int:
     ap.add_argument("--holdout-splits", type=int, default=6)
     args = ap.parse_args(argv)
     times, tiles = load(args.times)
-    mean, worst, a, p, full, params = fit(times, tiles)
-    print(f"# {len(times)} shapes; waves: part-filled last wave costs max({p:.2f}, {a:.2f} + {1 - a:.2f} * fill);"
-          + "".join(f" config {f} for config {c} from {n} {t[0]}x{t[1]} tiles;" for (c, f, t), n in zip(FULL_CHIP, full)))
+    mean, worst, a, p, params = fit(times, tiles)
+    print(f"# {len(times)} shapes; waves: part-filled last wave costs max({p:.2f}, {a:.2f} + {1 - a:.2f} * fill)")
     for cid in ALL:
         if cid in params:
             bm, bn = tiles[cid]
-            print(f"    {{{cid}, {params[cid][0]:.2f}, {params[cid][1]:.2f}}},  // {bm}x{bn}")
+            print(f"    {{{cid}, {params[cid][0]:.3f}, {params[cid][1]:.3f}}},  // {bm}x{bn}")
     print(f"# in sample: choice / fastest = x{mean:.4f} on average, x{worst:.3f} at worst")
     keys = sorted(times)
     for seed in range(args.holdout_splits):
@@ -184,8 +155,8 @@ def main(argv=None) -> int:
         rnd.shuffle(ks)
         train = {k: times[k] for k in ks[: len(ks) // 2]}
         test = {k: times[k] for k in ks[len(ks) // 2:]}
-        _, _, a_s, p_s, f_s, prm = fit(train, tiles)
-        m, w = regret(test, tiles, prm, a_s, p_s, f_s)
+        _, _, a_s, p_s, prm = fit(train, tiles)
+        m, w = regret(test, tiles, prm, a_s, p_s)
         print(f"# held-out split {seed}: x{m:.4f} on average, x{w:.3f} at worst")
     return 0
 
