@@ -147,12 +147,13 @@ def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
         PT.assert_parity(f"{shape} cfg21", PT.run_gpu(a, b, 0.5, config_id=21), ref)
 
 
-# The 16x16x32 kernels with B copied to LDS (config 28: 256x256, config 29:
-# 128x256) and their register-transpose twins (configs 25 and 26) pair the
-# same k in every MFMA and sum in the same order, so they give the same bits;
-# K covers 1 to 65 steps of 64, M and N ragged against the tile, the element
-# path included (N or K odd).
-@pytest.mark.parametrize("pair", [(28, 25), (29, 26)], ids=lambda p: f"{p[0]}vs{p[1]}")
+# The 16x16x32 kernels pair the same k in every MFMA and sum in the same
+# order, so they give the same bits: the 256x256 kernel with B copied to LDS
+# (config 28) and its register-transpose twin (config 25); the 128x256
+# kernel with its copies on separate waves (config 31) and the same plan with
+# the copies among the MFMAs (config 29).  K covers 1 to 65 steps of 64, M
+# and N ragged against the tile, the element path included (N or K odd).
+@pytest.mark.parametrize("pair", [(28, 25), (31, 29)], ids=lambda p: f"{p[0]}vs{p[1]}")
 @pytest.mark.parametrize("shape", [(256, 256, 8), (300, 520, 200), (257, 1031, 72), (1000, 1500, 704),
                                    (513, 777, 4160), (4097, 2048, 1000), (2048, 4096, 1031)],
                          ids=lambda s: "x".join(map(str, s)))
@@ -221,7 +222,7 @@ def test_empty_outputs(gsr):
     assert gsr.gemm_scale_relu(a2, b2, 0.5).shape == (4, 0)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 17, 18, 21, 22, 24, 25, 26, 28, 29])
+@pytest.mark.parametrize("cid", [-1, 5, 17, 18, 21, 22, 24, 25, 28, 29, 31])
 def test_c_aligned_to_8_not_16_bytes(gsr, orc, cid):
     """A and B 16-byte aligned, C only 8-byte aligned (4 elements into a 16-byte
     aligned buffer): the 128-bit stores need 16-byte aligned rows of C, so
@@ -261,7 +262,7 @@ def test_unaligned_pointers(gsr, orc, offset):
     PT.assert_parity(f"unaligned+{offset}", bits(cd.cpu()), ref)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 21, 24, 25, 26, 28, 29])
+@pytest.mark.parametrize("cid", [-1, 5, 21, 24, 25, 28, 29, 31])
 def test_guard_bands_and_full_coverage(gsr, orc, cid):
     """C sits inside a larger buffer filled with a sentinel: the bands before
     and after stay untouched and every element of C is written."""

@@ -19,7 +19,11 @@ and check them:
   lane i, element e comes from source lane 4e + i / 4, element i mod 4) and
   checks each fragment against the 16x16x32 operand layout, with both
   operands pairing the same k, and that the eight rows the LDS serves per
-  cycle sit on distinct banks.
+  cycle sit on distinct banks;
+* for configuration 31 (gsr_interleave16c.hpp), whose copies run on waves of
+  their own, a barrier-interval model of the two roles: every stage the MFMA
+  waves read in an interval has landed by the barrier that opens it, and no
+  copy writes a stage during an interval in which it is read.
 
 Planted mistakes in the plan (a copy before the barrier, an operand read too
 late) are caught by the model, so it is not vacuous.
@@ -240,3 +244,68 @@ def test_copy_and_read_addresses(struct):
                     for j in range(8):
                         assert alds[off + 2 * j] == (wm * wtm + 16 * b + lrow, 32 * ks + 8 * lch(lq) + j)
     assert extra_bank_cycles == 0
+
+
+# ---- the copy-wave protocol (configuration 31, gsr_interleave16c.hpp) -----------
+
+def copy_wave_program(ksteps: int, a_before_barrier: bool = False, wait=8) -> list:
+    """Copy waves' issue order: stage 0 and 1 copies, wait, prologue barrier;
+    per K-step t the B(t+2) copies, the wait, barrier b_t and the A(t+2)
+    copies; then a full drain and the epilogue's barrier."""
+    ev = [("copy", "A", 0, 0)] * 4 + [("copy", "B", 0, 0)] * 8 + [("copy", "A", 1, 1)] * 4 + [("copy", "B", 1, 1)] * 8
+    ev += [("wait", 12), ("barrier",)]
+    for t in range(ksteps):
+        ev += [("copy", "B", (t + 2) % 3, t + 2)] * 8
+        if a_before_barrier:
+            ev += [("copy", "A", t % 2, t + 2)] * 4
+        ev += [("wait", wait), ("barrier",)]
+        if not a_before_barrier:
+            ev += [("copy", "A", t % 2, t + 2)] * 4
+    return ev + [("wait", 0), ("barrier",)]
+
+
+def mfma_wave_reads(ksteps: int) -> list:
+    """MFMA waves' stage reads per barrier interval: (interval, operand,
+    stage, K-step of the data).  Interval j follows the j-th barrier of the
+    kernel (the prologue's is the first, b_t the (t+2)-th)."""
+    reads = [(1, "A", 0, 0), (1, "B", 0, 0)]  # step 0's substep-0 operands
+    for t in range(ksteps):
+        reads += [(t + 1, "A", t % 2, t), (t + 1, "B", t % 3, t)]                    # substep 0, for substep 1
+        reads += [(t + 2, "A", (t + 1) % 2, t + 1), (t + 2, "B", (t + 1) % 3, t + 1)]  # after b_t
+    return reads
+
+
+def check_copy_waves(ksteps: int, **kw) -> None:
+    ev = copy_wave_program(ksteps, **kw)
+    interval, in_flight = 0, []
+    landed = {}           # (operand, stage) -> K-step whose copies have landed
+    landed_at = {}        # barrier index -> snapshot of landed data at that barrier
+    written_in = {}       # interval -> set of (operand, stage) copied into during it
+    for e in ev:
+        if e[0] == "copy":
+            in_flight.append(e[1:])
+            written_in.setdefault(interval, set()).add((e[1], e[2]))
+            landed.pop((e[1], e[2]), None)
+        elif e[0] == "wait":
+            while len(in_flight) > e[1]:
+                op, st, step = in_flight.pop(0)
+                landed[(op, st)] = step
+        else:
+            interval += 1
+            landed_at[interval] = dict(landed)
+    assert interval == ksteps + 2, "copy and MFMA waves pass the same number of barriers"
+    for j, op, st, step in mfma_wave_reads(ksteps):
+        assert landed_at[j].get((op, st)) == step, f"{op} stage {st} read in interval {j} before step {step} landed"
+        assert (op, st) not in written_in.get(j, set()), f"{op} stage {st} copied into while it is read (interval {j})"
+
+
+@pytest.mark.parametrize("ksteps", [2, 4, 6, 8, 14])
+def test_copy_wave_protocol(ksteps):
+    check_copy_waves(ksteps)
+
+
+@pytest.mark.parametrize("mistake", [{"a_before_barrier": True}, {"wait": 12}],
+                         ids=["A-copies-before-the-barrier", "wait-too-loose"])
+def test_copy_wave_model_catches_planted_mistakes(mistake):
+    with pytest.raises(AssertionError):
+        check_copy_waves(8, **mistake)

@@ -19,8 +19,8 @@
 #include "gsr_kspec.hpp"
 #include "gsr_interleave_q.hpp"
 #include "gsr_interleave16.hpp"
-#include "gsr_interleave16h.hpp"
 #include "gsr_interleave16d.hpp"
+#include "gsr_interleave16c.hpp"
 
 namespace {
 
@@ -69,10 +69,11 @@ hipError_t launch_ilv16d(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilv16d_kernel<T>, dim3(grid), dim3(T::NT), s, p);
 }
 
-hipError_t launch_ilv16h(const Problem& p, int grid, hipStream_t s)
+hipError_t launch_ilv16c(const Problem& p, int grid, hipStream_t s)
 {
-    return launch_kernel(gsr::gemm_scale_relu_ilv16h_kernel, dim3(grid), dim3(gsr::Ilv16HCfg::NT), s, p);
+    return launch_kernel(gsr::gemm_scale_relu_ilv16c_kernel, dim3(grid), dim3(gsr::Ilv16CCfg::NT), s, p);
 }
+
 
 
 hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
@@ -137,11 +138,12 @@ struct Entry {
 
 // The compiled tile table, by id.  Ids are stable from one library version to
 // the next, so a tuning table written earlier keeps its meaning; the ids of
-// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23: tiles
-// that neither the selector nor any measured tuning entry chose; 15 and 23,
-// the 256x256 and 128x256 tiles on 32x32x16 MFMAs, were slower than
-// configurations 28 and 29 on every measured shape) are not reused and are
-// rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is
+// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23, 26:
+// tiles that neither the selector nor any measured tuning entry chose; 15 and
+// 23, the 256x256 and 128x256 tiles on 32x32x16 MFMAs, were slower than
+// configurations 28 and 29 on every measured shape; 26, the 128x256 tile with
+// B transposed through registers, is served by 29 and 31) are not reused and
+// are rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is
 // made by select().
 const Entry kTable[] = {
     GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
@@ -159,15 +161,15 @@ const Entry kTable[] = {
     // registers: configuration 28's twin (same bits), kept for comparison; chip rounds of
     // 16 x 16 tiles where the grid divides into them
     GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16, 2),
-    // 128x256 on the 16x16x32 MFMA (8 x 4 blocks of 16x16 per wave), B transposed through
-    // registers: configuration 29's twin (same bits), kept for comparison
-    GSR_ILV(26, 128, 256, gsr::Ilv16HCfg::LDS_BYTES, launch_ilv16h, 1),
     // configuration 25 with B copied to LDS as stored and read with transpose reads: the
     // selector's 256x256 tile
     GSR_ILV(28, 256, 256, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16DCfg>, 2),
-    // configuration 26 with B copied to LDS as stored and read with transpose reads: the
-    // selector's 128x256 tile
+    // configuration 28's kernel on the 128x256 tile (8 x 4 blocks of 16x16 per wave):
+    // configuration 31's twin (same bits), kept for comparison
     GSR_ILV(29, 128, 256, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
+    // configuration 29 with its copies issued by four extra copy waves (512 threads): the
+    // selector's 128x256 tile
+    GSR_ILV(31, 128, 256, gsr::Ilv16CCfg::LDS_BYTES, launch_ilv16c, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -184,11 +186,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.70, 0.60 + 0.40 * fill) of a full one (a part-filled chip
+// full costs max(0.75, 0.60 + 0.40 * fill) of a full one (a part-filled chip
 // runs at a higher power-limited clock, but every tile still pays its fixed
 // cost).  The 256x256 and 128x256 tiles have one candidate each, the
-// 16x16x32 kernels with B copied to LDS (configurations 28 and 29): each was
-// faster than every other kernel of its tile on every measured shape.  The
+// 16x16x32 kernels with B copied to LDS (configuration 28, and configuration
+// 31 with its copies on separate waves): each was faster than every other
+// kernel of its tile on every measured shape.  The
 // rates, overheads and the partial-wave form were fitted (least squares in
 // relative error for the rates, then the grid point whose choices come
 // closest to the fastest configuration) to the times of every configuration
@@ -197,7 +200,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // benchmark workloads), the offline sweep the aikraft.ru guide describes in
 // sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
-// choice is on average within 0.1 % of the fastest configuration, 2.1 % at
+// choice is on average within 0.05 % of the fastest configuration, 3.0 % at
 // worst.  Below K = 256 the four-wave K-split tiles replace their copy-wave
 // twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
@@ -206,18 +209,18 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {28, 6.086, 10.619},  // 256x256, 16x16x32, B copied to LDS
-    {29, 5.444, 7.450},   // 128x256, 16x16x32, B copied to LDS
-    {24, 3.341, 5.804},   // 128x128, explicit interleave
-    {5, 3.807, 9.881},    // 256x128
-    {10, 1.971, 5.517},   // 64x128
-    {8, 2.345, 5.344},    // 128x64
-    {21, 2.785, 3.523},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.822, 2.592},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.512, 4.101},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.656, 3.130},   // 32x64, K split, four waves       (K <= 256)
+    {28, 6.363, 9.611},   // 256x256, 16x16x32, B copied to LDS
+    {31, 6.228, 6.550},   // 128x256, 16x16x32, B copied to LDS by copy waves
+    {24, 3.451, 5.287},   // 128x128, explicit interleave
+    {5, 3.909, 8.974},    // 256x128
+    {10, 1.968, 5.092},   // 64x128
+    {8, 2.355, 5.036},    // 128x64
+    {21, 2.878, 3.550},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.837, 2.620},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.571, 3.999},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.666, 3.126},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.70, kPartA = 0.60;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr double kPartMin = 0.75, kPartA = 0.60;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 
 int select(int64_t M, int64_t N, int64_t K)
 {
@@ -340,7 +343,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 700; }
+int gsr_version(void) { return 710; }
 
 const char* gsr_status_string(int status)
 {

@@ -17,7 +17,7 @@
 // One barrier per K-step publishes the next step's buffers and frees the
 // current ones.  The kernels on this design: 128x128 tiles on 32x32x16
 // MFMAs (gsr_interleave_q.hpp), 256x256 and 128x256 tiles on 16x16x32 MFMAs
-// (gsr_interleave16.hpp, gsr_interleave16h.hpp, gsr_interleave16d.hpp).
+// (gsr_interleave16.hpp, gsr_interleave16d.hpp, gsr_interleave16c.hpp).
 //
 // Ragged edges: rows of A past M and rows of B past K fall outside the
 // advancing descriptors (read as zero); B columns past N and A columns past K

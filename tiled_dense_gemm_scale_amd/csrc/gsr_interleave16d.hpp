@@ -3,8 +3,9 @@
 // unit: 256x256 tiles (configuration 28) and 128x256 tiles (configuration 29).
 //
 // Waves, accumulators, A path, A^T fragments, launch order and epilogue are
-// those of the register-transpose kernels in gsr_interleave16.hpp (256x256)
-// and gsr_interleave16h.hpp (128x256).  What changes is B: instead of
+// those of the register-transpose kernel in gsr_interleave16.hpp (256x256;
+// the 128x256 tile is the same at half the height: four waves of 64x128,
+// 8 (n) x 4 (m) accumulator blocks each).  What changes is B: instead of
 // loading an 8x8 block per thread into registers, transposing it with byte
 // permutes and writing B^T rows to LDS, the buffer unit copies B straight
 // into LDS as it is stored (64 k-rows of 256 n, 512 bytes each), and each
@@ -74,9 +75,10 @@ struct Ilv16DCfg : Ilv16Cfg {
     static constexpr int AC0 = 8, ACD = 7;              // A copies in substep 1: first slot, stride
 };
 
-// The 128x256 tile (configuration 29): four waves of 64x128, 8 (n) x 4 (m)
-// blocks of 16x16 per wave, 32 MFMAs per substep; A stages of 16 KiB, B
-// stages as above (2 x 16 + 3 x 32 = 128 KiB).
+// The 128x256 tile (configuration 29; gsr_interleave16c.hpp runs the same
+// plan with its copies on separate waves, configuration 31): four waves of
+// 64x128, 8 (n) x 4 (m) blocks of 16x16 per wave, 32 MFMAs per substep; A
+// stages of 16 KiB, B stages as above (2 x 16 + 3 x 32 = 128 KiB).
 struct Ilv16HDCfg {
     static constexpr int BM = 128, BN = 256, BK = 64, WM = 2, WN = 2;
     static constexpr int NW = WM * WN, NT = kWave * NW;
