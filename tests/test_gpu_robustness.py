@@ -48,7 +48,7 @@ def test_largest_operand_under_2gib(gsr, orc, K):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cid", [25, 28, 29, 31])
+@pytest.mark.parametrize("cid", [25, 28, 29, 31, 32])
 def test_largest_operand_under_2gib_interleaved(gsr, orc, cid):
     """The same A just under 2^31 bytes through each interleaved 256x256 and
     128x256 kernel, forced: their per-lane copy offsets are formed from base

@@ -26,10 +26,11 @@ def gsr(native):
 
 @pytest.mark.parametrize("cid,shape", [(28, (4097, 700, 264)), (16, (700, 1100, 264)), (8, (700, 1100, 264)),
                                        (18, (700, 1100, 264)), (21, (700, 1100, 264)), (22, (700, 1100, 264)),
-                                       (24, (700, 1100, 264)), (25, (700, 1100, 264)), (29, (700, 1100, 264)),
+                                       (25, (700, 1100, 264)), (29, (700, 1100, 264)),
                                        (25, (4096, 4096, 136)), (25, (8192, 4096, 72)), (28, (4096, 8192, 72)),
                                        (28, (700, 1100, 264)), (28, (4096, 4096, 136)), (31, (700, 1100, 264)),
-                                       (31, (2048, 4096, 200))],
+                                       (31, (2048, 4096, 200)),
+                                       (32, (700, 1100, 264)), (32, (2048, 2048, 200))],
                          ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_launch_order_does_not_change_results(gsr, orc, cid, shape):
     """Every launch order, including the chip rounds of 16 x 16 tiles (order 2,

@@ -34,24 +34,49 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HDR = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc", "gsr_interleave16d.hpp")
+CSRC = os.path.join(ROOT, "tiled_dense_gemm_scale_amd", "csrc")
+HDR = os.path.join(CSRC, "gsr_interleave16d.hpp")
+HDR_C = os.path.join(CSRC, "gsr_interleave16c.hpp")
 
-# tile shapes of the two instantiations (four waves of 2 x 2 in both)
+# tile shapes of the instantiations (four MFMA waves of 2 x 2 in all)
 TILES = {"Ilv16DCfg": (256, 256), "Ilv16HDCfg": (128, 256)}
+COPY_WAVE_TILES = {"Ilv16CCfg": (128, 256), "Ilv16QCCfg": (128, 128)}
 SLOT_KEYS = ("X7_0", "X7_1", "Y0_0", "Y0_1", "BAR", "BC0", "BCD", "AC0", "ACD")
+COPY_WAVE_KEYS = ("X7_0", "X7_1", "Y0_0", "Y0_1", "YS", "BAR")
 
 
-def plan(struct: str) -> dict:
-    """The slot constants of one tile configuration, read from the header."""
-    src = open(HDR).read()
+def _constants(header: str, struct: str, keys) -> dict:
+    """Integer constants of one configuration struct; a value written as
+    Other::KEY is looked up in struct Other (in this header or the
+    B-through-LDS one)."""
+    src = open(header).read()
     body = src[src.index(f"struct {struct}"):]
     body = body[: body.index("};")]
     c = {}
-    for key in SLOT_KEYS:
-        m = re.search(rf"\b{key} = (\d+)", body)
+    for key in keys:
+        m = re.search(rf"\b{key} = (\w+)(?:::(\w+))?", body)
         assert m, (struct, key)
-        c[key] = int(m.group(1))
-    bm, bn = TILES[struct]
+        if m.group(2) is None:
+            c[key] = int(m.group(1))
+        else:
+            other = header if f"struct {m.group(1)}" in src else HDR
+            c[key] = _constants(other, m.group(1), (m.group(2),))[m.group(2)]
+    return c
+
+
+def plan(struct: str) -> dict:
+    """The slot constants of one tile configuration, read from the header.
+    For the copy-wave kernels the copies are placed where the copy waves
+    issue them relative to the barriers: B(t+2) before any read of substep 0
+    (right after b_{t-1}), A(t+2) right after b_t."""
+    if struct in COPY_WAVE_TILES:
+        c = _constants(HDR_C, struct, COPY_WAVE_KEYS)
+        bm, bn = COPY_WAVE_TILES[struct]
+        c.update(BC0=0, BCD=1, AC0=c["BAR"], ACD=1)
+    else:
+        c = _constants(HDR, struct, SLOT_KEYS)
+        c["YS"] = 4
+        bm, bn = TILES[struct]
     c["FM"], c["FN"] = bm // 2 // 16, bn // 2 // 16
     c["A_PER"], c["B_PER"] = bm * 64 * 2 // 1024 // 4, bn * 64 * 2 // 1024 // 4
     return c
@@ -77,15 +102,15 @@ def program(c: dict, ksteps: int) -> list:
             ev.append(("readX", i // FM - 1, i % FM, br, t, kr))
         if i in (x7, x7 + 1):
             ev.append(("readX", FN - 1, i - x7, br, t, kr))
-        if y0 <= i < y0 + 4 * FM and (i - y0) % 4 == 0:
-            ev.append(("readY", (i - y0) // 4, sr, t, kr))
+        if y0 <= i < y0 + c["YS"] * FM and (i - y0) % c["YS"] == 0:
+            ev.append(("readY", (i - y0) // c["YS"], sr, t, kr))
 
     for t in range(ksteps):
         sa, sb = t % 2, t % 3
         for i in range(slots):
             ev.append(("mma", i, t, 0))
             reads(i, sa, sb, t, 1, c["Y0_0"], c["X7_0"])
-            if i >= c["BC0"] and (i - c["BC0"]) % c["BCD"] == 0:
+            if i >= c["BC0"] and (i - c["BC0"]) % c["BCD"] == 0 and (i - c["BC0"]) // c["BCD"] < c["B_PER"]:
                 ev.append(("copyB", (t + 2) % 3, t + 2))
         for i in range(slots):
             ev.append(("mma", i, t, 1))
@@ -144,7 +169,7 @@ def check_program(c: dict, ksteps: int) -> None:
             assert Y.get((ks, b)) == (t, ks), f"MFMA slot {i} of step {t} substep {ks} sees A^T fragment {Y.get((ks, b))}"
 
 
-@pytest.mark.parametrize("struct", sorted(TILES))
+@pytest.mark.parametrize("struct", sorted(TILES) + sorted(COPY_WAVE_TILES))
 @pytest.mark.parametrize("ksteps", [2, 4, 6, 8, 14])
 def test_slot_plan_is_consistent(struct, ksteps):
     check_program(plan(struct), ksteps)
@@ -178,21 +203,24 @@ def swz_a(r):
     return (r ^ (r >> 3)) & 7
 
 
-@pytest.mark.parametrize("struct", sorted(TILES))
-def test_copy_and_read_addresses(struct):
-    bm, bn = TILES[struct]
+@pytest.mark.parametrize("tile", [(256, 256), (128, 256), (128, 128)], ids=lambda t: f"{t[0]}x{t[1]}")
+def test_copy_and_read_addresses(tile):
+    """Copy waves or MFMA waves alike: copier w = 0..3 (the wave, or the copy
+    wave's index) fills 1 KiB blocks w + 4i."""
+    bm, bn = tile
     bk, nw, rowb = 64, 4, bn * 2
     wtm, wtn = bm // 2, bn // 2
+    cpr, rpk, cpw = bn // 8, 1024 // rowb, wtn // 8  # chunks per B row, rows per copy, chunks per wave
     a_per, b_per = bm * bk * 2 // 1024 // nw, bn * bk * 2 // 1024 // nw
-    # B copies: copy i of wave w fills chunk positions 64 (w + 4i) + lane
+    # B copies: copy i of copier w fills chunk positions 64 (w + 4i) + lane
     blds = {}
     for w in range(nw):
         for i in range(b_per):
             for lane in range(64):
-                k = 2 * w + 8 * i + (lane >> 5)
-                c = (lane & 31) ^ fb16(k)
+                k = rpk * (w + nw * i) + lane // cpr
+                c = (lane % cpr) ^ fb16(k)
                 base = 1024 * (w + nw * i) + 16 * lane
-                assert base == k * rowb + (lane & 31) * 16
+                assert base == k * rowb + (lane % cpr) * 16
                 for e in range(8):
                     blds[base + 2 * e] = (k, 8 * c + e)
     assert sorted(blds.values()) == sorted((k, n) for k in range(bk) for n in range(bn))
@@ -221,7 +249,7 @@ def test_copy_and_read_addresses(struct):
                         g, li = lane >> 4, lane & 15
                         e, q = li >> 2, li & 3
                         krow0 = 8 * lch(g) + e
-                        xa = krow0 * rowb + (16 * wn + (q >> 1)) * 16 + (q & 1) * 8 + ((a ^ (fb16(krow0) >> 1)) << 5)
+                        xa = krow0 * rowb + (((cpw * wn + 2 * a + (q >> 1)) ^ fb16(krow0)) << 4) + (q & 1) * 8
                         addr.append(xa + ks * 32 * rowb + rd * 4 * rowb)
                     for lane in range(64):
                         g, i = lane >> 4, lane & 15

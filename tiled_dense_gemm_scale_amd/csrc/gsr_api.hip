@@ -17,7 +17,6 @@
 #include "gsr_interleave.hpp"
 #include "gsr_ksplit.hpp"
 #include "gsr_kspec.hpp"
-#include "gsr_interleave_q.hpp"
 #include "gsr_interleave16.hpp"
 #include "gsr_interleave16d.hpp"
 #include "gsr_interleave16c.hpp"
@@ -69,17 +68,14 @@ hipError_t launch_ilv16d(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilv16d_kernel<T>, dim3(grid), dim3(T::NT), s, p);
 }
 
+template <class T>
 hipError_t launch_ilv16c(const Problem& p, int grid, hipStream_t s)
 {
-    return launch_kernel(gsr::gemm_scale_relu_ilv16c_kernel, dim3(grid), dim3(gsr::Ilv16CCfg::NT), s, p);
+    return launch_kernel(gsr::gemm_scale_relu_ilv16c_kernel<T>, dim3(grid), dim3(T::NT), s, p);
 }
 
 
 
-hipError_t launch_ilvq(const Problem& p, int grid, hipStream_t s)
-{
-    return launch_kernel(gsr::gemm_scale_relu_ilvq_kernel, dim3(grid), dim3(256), s, p);
-}
 
 template <int BM, int BN, int S>
 hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
@@ -138,13 +134,13 @@ struct Entry {
 
 // The compiled tile table, by id.  Ids are stable from one library version to
 // the next, so a tuning table written earlier keeps its meaning; the ids of
-// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23, 26:
-// tiles that neither the selector nor any measured tuning entry chose; 15 and
-// 23, the 256x256 and 128x256 tiles on 32x32x16 MFMAs, were slower than
-// configurations 28 and 29 on every measured shape; 26, the 128x256 tile with
-// B transposed through registers, is served by 29 and 31) are not reused and
-// are rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice per shape class is
-// made by select().
+// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23, 24, 26:
+// tiles that neither the selector nor any measured tuning entry chose; 15, 23
+// and 24, the 256x256, 128x256 and 128x128 tiles on 32x32x16 MFMAs, were
+// slower than configurations 28, 29 and 32 on every measured shape; 26, the
+// 128x256 tile with B transposed through registers, is served by 29 and 31)
+// are not reused and are rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice
+// per shape class is made by select().
 const Entry kTable[] = {
     GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
     GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
@@ -155,8 +151,6 @@ const Entry kTable[] = {
     // K split with separate copy waves (eight waves per workgroup), two steps ahead
     GSR_KSPEC(21, 64, 64, 4, 2, 4),
     GSR_KSPEC(22, 32, 64, 4, 2, 4),
-    // explicit interleave at a quarter of 256x256, 4 waves of 64x64
-    GSR_ILV(24, 128, 128, gsr::IlvQCfg::LDS_BYTES, launch_ilvq, 1),
     // 256x256 on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave), B transposed through
     // registers: configuration 28's twin (same bits), kept for comparison; chip rounds of
     // 16 x 16 tiles where the grid divides into them
@@ -169,7 +163,10 @@ const Entry kTable[] = {
     GSR_ILV(29, 128, 256, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
     // configuration 29 with its copies issued by four extra copy waves (512 threads): the
     // selector's 128x256 tile
-    GSR_ILV(31, 128, 256, gsr::Ilv16CCfg::LDS_BYTES, launch_ilv16c, 1),
+    GSR_ILV(31, 128, 256, gsr::Ilv16CCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16CCfg>, 1),
+    // the same kernel on the 128x128 tile (B rows of 256 bytes, 4 x 4 blocks per MFMA wave):
+    // the selector's 128x128 tile
+    GSR_ILV(32, 128, 128, gsr::Ilv16QCCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16QCCfg>, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -186,12 +183,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.75, 0.60 + 0.40 * fill) of a full one (a part-filled chip
+// full costs max(0.60, 0.55 + 0.45 * fill) of a full one (a part-filled chip
 // runs at a higher power-limited clock, but every tile still pays its fixed
-// cost).  The 256x256 and 128x256 tiles have one candidate each, the
-// 16x16x32 kernels with B copied to LDS (configuration 28, and configuration
-// 31 with its copies on separate waves): each was faster than every other
-// kernel of its tile on every measured shape.  The
+// cost).  The 256x256, 128x256 and 128x128 tiles have one candidate each, the
+// 16x16x32 kernels with B copied to LDS (configuration 28, and configurations
+// 31 and 32 with their copies on separate waves): each was faster than every
+// other kernel of its tile on every measured shape.  The
 // rates, overheads and the partial-wave form were fitted (least squares in
 // relative error for the rates, then the grid point whose choices come
 // closest to the fastest configuration) to the times of every configuration
@@ -200,7 +197,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // benchmark workloads), the offline sweep the aikraft.ru guide describes in
 // sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
-// choice is on average within 0.05 % of the fastest configuration, 3.0 % at
+// choice is on average within 0.12 % of the fastest configuration, 4.3 % at
 // worst.  Below K = 256 the four-wave K-split tiles replace their copy-wave
 // twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
@@ -209,18 +206,18 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {28, 6.363, 9.611},   // 256x256, 16x16x32, B copied to LDS
-    {31, 6.228, 6.550},   // 128x256, 16x16x32, B copied to LDS by copy waves
-    {24, 3.451, 5.287},   // 128x128, explicit interleave
-    {5, 3.909, 8.974},    // 256x128
-    {10, 1.968, 5.092},   // 64x128
-    {8, 2.355, 5.036},    // 128x64
-    {21, 2.878, 3.550},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.837, 2.620},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.571, 3.999},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.666, 3.126},   // 32x64, K split, four waves       (K <= 256)
+    {28, 5.821, 13.108},  // 256x256, 16x16x32, B copied to LDS
+    {31, 5.759, 8.723},   // 128x256, 16x16x32, B copied to LDS by copy waves
+    {32, 3.733, 4.850},   // 128x128, 16x16x32, B copied to LDS by copy waves
+    {5, 3.735, 12.205},   // 256x128
+    {10, 1.996, 6.495},   // 64x128
+    {8, 2.377, 6.225},    // 128x64
+    {21, 2.786, 3.654},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.834, 2.719},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.513, 4.233},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.673, 3.293},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.75, kPartA = 0.60;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr double kPartMin = 0.60, kPartA = 0.55;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 
 int select(int64_t M, int64_t N, int64_t K)
 {
@@ -343,7 +340,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 710; }
+int gsr_version(void) { return 720; }
 
 const char* gsr_status_string(int status)
 {

@@ -65,13 +65,13 @@ __device__ __forceinline__ void mfma16_inplace(f32x4& acc, const half8& x, const
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
 }
 
-// Epilogue of the 16x16 layout, for a WTM x 128 wave sub-tile: lane l holds,
-// for accumulator block (a, b), rows m = 16b + l % 16 and columns
-// n = 16a + 4(l / 16) + 0..3 of the sub-tile.  Scale, ReLU (or the variant)
-// and round in registers, stage each wave's fp16 sub-tile in its own LDS
-// rows (16-byte chunk c of row r at physical chunk c ^ (r % 16)), then store
-// whole 256-byte row segments.  Called once every wave's copies have been
-// drained.
+// Epilogue of the 16x16 layout, for a WTM x WTN wave sub-tile (WTN = 128 or
+// 64): lane l holds, for accumulator block (a, b), rows m = 16b + l % 16 and
+// columns n = 16a + 4(l / 16) + 0..3 of the sub-tile.  Scale, ReLU (or the
+// variant) and round in registers, stage each wave's fp16 sub-tile in its own
+// LDS rows (16-byte chunk c of row r at physical chunk c ^ (r mod WTN / 8)),
+// then store whole row segments of 2 WTN bytes.  Called once every wave's
+// copies have been drained.
 template <class T>
 __device__ __forceinline__ void ilv16_epilogue_t(const Problem& p, const f32x4 (&acc)[T::FN][T::FM], uint8_t* smem,
                                                  int m0, int n0, int wm, int wn, int wave)
@@ -80,8 +80,9 @@ __device__ __forceinline__ void ilv16_epilogue_t(const Problem& p, const f32x4 (
     const uint32_t lane = (uint32_t)(threadIdx.x & 63);
     const uint32_t lrow = lane & 15u, lq = lane >> 4;
     const uint32_t N = (uint32_t)p.N;
-    constexpr uint32_t CPR = T::WTN / 8, RB = T::WTN * 2;  // 16 chunks, 256 bytes per staging row
-    static_assert(T::WTN == 128 && T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES, "staging rows of 16 chunks fit");
+    constexpr uint32_t CPR = T::WTN / 8, RB = T::WTN * 2;  // chunks and bytes per staging row
+    static_assert((T::WTN == 128 || T::WTN == 64) && T::NW * T::WTM * T::WTN * 2 <= T::LDS_BYTES,
+                  "staging rows of 8 or 16 chunks fit");
     const bool plain = plain_epilogue(p);
     f32x4 bvs[FN];
     {

@@ -34,6 +34,7 @@
 
 namespace gsr {
 
+// The 128x256 tile (configuration 31).
 struct Ilv16CCfg {
     static constexpr int BM = 128, BN = 256, BK = 64, WM = 2, WN = 2;
     static constexpr int NW = WM * WN;                   // MFMA waves (0..3)
@@ -49,19 +50,49 @@ struct Ilv16CCfg {
     static constexpr int B_PER = B_BYTES / 1024 / NCW;   // 8
     static constexpr int LDS_BYTES = 2 * A_BYTES + 3 * B_BYTES;  // 128 KiB
     static constexpr int SLOTS = FM * FN;                // 32 MFMAs per substep
-    // configuration 29's read plan
+    // configuration 29's read plan: X[7] at X7_0 / X7_1, Y[b] at Y0 + YS b
     static constexpr int X7_0 = Ilv16HDCfg::X7_0, X7_1 = Ilv16HDCfg::X7_1;
-    static constexpr int Y0_0 = Ilv16HDCfg::Y0_0, Y0_1 = Ilv16HDCfg::Y0_1, BAR = Ilv16HDCfg::BAR;
-    static_assert(FM == 4 && FN == 8 && A_PER == 4 && B_PER == 8, "the plans below");
-    static_assert(FM >= BAR && Y0_1 >= BAR && X7_1 >= BAR, "reads of the new stages follow the barrier");
+    static constexpr int Y0_0 = Ilv16HDCfg::Y0_0, Y0_1 = Ilv16HDCfg::Y0_1, YS = 4, BAR = Ilv16HDCfg::BAR;
 };
 
+// The 128x128 tile (configuration 32): four MFMA waves of 64x64, 4 (n) x 4
+// (m) blocks of 16x16 each, 16 MFMAs per substep; B rows of 256 bytes (16
+// chunks, the same fb16 swizzle); A and B stages of 16 KiB (2 + 3 = 80 KiB).
+// Reads: the last B^T fragment at slots 1-2 of substep 0 and 2-3 of substep
+// 1, the A^T fragments every second slot from 0 and from 1, the barrier at
+// slot 1 of substep 1.
+struct Ilv16QCCfg {
+    static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2;
+    static constexpr int NW = WM * WN;                   // MFMA waves (0..3)
+    static constexpr int NCW = 4;                        // copy waves (4..7)
+    static constexpr int NT = kWave * (NW + NCW);        // 512 threads
+    static constexpr int CH = BK / 8;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;   // 64 x 64 per MFMA wave
+    static constexpr int FM = WTM / 16, FN = WTN / 16;   // 4 (m) x 4 (n) blocks of 16x16
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int B_REGION = 2 * A_BYTES;
+    static constexpr int ROWB = BN * 2;
+    static constexpr int A_PER = A_BYTES / 1024 / NCW;   // 4 copies per copy wave per step
+    static constexpr int B_PER = B_BYTES / 1024 / NCW;   // 4
+    static constexpr int LDS_BYTES = 2 * A_BYTES + 3 * B_BYTES;  // 80 KiB
+    static constexpr int SLOTS = FM * FN;                // 16 MFMAs per substep
+    static constexpr int X7_0 = 1, X7_1 = 2;
+    static constexpr int Y0_0 = 0, Y0_1 = 1, YS = 2, BAR = 1;
+};
+
+template <class T>
 __global__ void __launch_bounds__(512) gemm_scale_relu_ilv16c_kernel(Problem p)
 {
-    using T = Ilv16CCfg;
     constexpr int BK = T::BK, CH = T::CH, FM = T::FM, FN = T::FN;
+    constexpr uint32_t CPR = T::BN / 8, RPK = 1024 / T::ROWB;  // chunks per B row, B rows per 1 KiB copy
+    static_assert(BK == 64 && (T::BN == 256 || T::BN == 128) && T::WTN == T::BN / 2 && T::BM == 128,
+                  "the copy and read plans below");
+    static_assert(T::A_PER == 4 && T::NW == 4 && T::NCW == 4, "the copy plans below");
     static_assert(T::LDS_BYTES <= 163840, "LDS budget of one workgroup on gfx950");
     static_assert(T::B_BYTES + 32 * T::ROWB + 4 * T::ROWB < 65536, "B read offsets fit the immediate field");
+    static_assert(FM >= T::BAR && T::Y0_1 >= T::BAR && T::X7_1 >= T::BAR, "reads of the new stages follow the barrier");
+    static_assert(T::X7_0 + 1 < FM * (FN - 1) && T::Y0_0 + T::YS * (FM - 1) < T::SLOTS && T::Y0_1 + T::YS * (FM - 1) < T::SLOTS,
+                  "operands of the next substep are read within this one");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];  // A0 | A1 | B0 | B1 | B2
 
@@ -103,13 +134,14 @@ __global__ void __launch_bounds__(512) gemm_scale_relu_ilv16c_kernel(Problem p)
         const uint32_t av0 = arow + 16u * c0, av1 = arow + 32u * K * 2u + 16u * (c0 ^ 4u);
         const uint32_t kc0 = 8u * c0, kc1 = 8u * (c0 ^ 4u);
         const uint32_t a_istride = 64u * K * 2u;
-        // B: copy i fills chunk positions 64 (cw + 4i) + lane: row
-        // k = 2 cw + 8 i + lane / 32, logical chunk (lane % 32) ^ fb16(k)
+        // B: copy i fills chunk positions 64 (cw + 4i) + lane of the stage:
+        // row k = RPK (cw + 4i) + lane / CPR, logical chunk
+        // (lane % CPR) ^ fb16(k) (fb16 touches chunk bits 1-3 only)
         uint32_t b_voff[T::B_PER];
 #pragma unroll
         for (int i = 0; i < T::B_PER; ++i) {
-            const uint32_t k = 2u * cw + 8u * (uint32_t)i + ((uint32_t)lane >> 5);
-            const uint32_t c = ((uint32_t)lane & 31u) ^ fb16(k);
+            const uint32_t k = RPK * (cw + 4u * (uint32_t)i) + (uint32_t)lane / CPR;
+            const uint32_t c = ((uint32_t)lane & (CPR - 1u)) ^ fb16(k);
             b_voff[i] = ((uint32_t)n0 + 8u * c < N) ? (k * N + 8u * c) * 2u : kOutOfRange;
         }
         auto copy_a = [&](uint32_t stage, uint32_t k) {
@@ -158,15 +190,25 @@ __global__ void __launch_bounds__(512) gemm_scale_relu_ilv16c_kernel(Problem p)
         yb[b] = ry * (BK * 2) + ((lch ^ swz_a<CH>(ry)) << 4);
     }
     // B^T fragment a by transpose reads, B stage 0 (stage 1 rides in the
-    // immediate, stage 2 is added when read)
+    // immediate, stage 2 is added when read): logical chunk
+    // (WTN / 8) wn + 2a + q / 2 of row 8 lch(g) + e sits at physical chunk
+    // (that) ^ fb16(row)
     uint32_t xa[FN];
     {
         const uint32_t e = lrow >> 2, q = lrow & 3u;
         const uint32_t krow0 = 8u * lch + e;
-        const uint32_t h = fb16(krow0) >> 1;
-        const uint32_t base = (uint32_t)T::B_REGION + krow0 * T::ROWB + (16u * (uint32_t)wn + (q >> 1)) * 16u + (q & 1u) * 8u;
+        const uint32_t f = fb16(krow0);
+        if constexpr (T::WTN == 128) {  // the XOR stays inside the wave's 16 chunks
+            const uint32_t base = (uint32_t)T::B_REGION + krow0 * T::ROWB + (16u * (uint32_t)wn + (q >> 1)) * 16u + (q & 1u) * 8u;
 #pragma unroll
-        for (int a = 0; a < FN; ++a) xa[a] = base + ((((uint32_t)a) ^ h) << 5);
+            for (int a = 0; a < FN; ++a) xa[a] = base + ((((uint32_t)a) ^ (f >> 1)) << 5);
+        } else {
+#pragma unroll
+            for (int a = 0; a < FN; ++a) {
+                const uint32_t chunk = ((uint32_t)(T::WTN / 8) * (uint32_t)wn + 2u * (uint32_t)a + (q >> 1)) ^ f;
+                xa[a] = (uint32_t)T::B_REGION + krow0 * T::ROWB + (chunk << 4) + (q & 1u) * 8u;
+            }
+        }
     }
 
     f32x4 acc[FN][FM];
@@ -195,11 +237,14 @@ __global__ void __launch_bounds__(512) gemm_scale_relu_ilv16c_kernel(Problem p)
     auto read_y = [&](int S, int ks, int b, half8& dst) {
         dst = __builtin_bit_cast(half8, *(const u32x4*)(smem + S * T::A_BYTES + (yb[b] ^ (ks ? 64u : 0u))));
     };
-    // reads of slot i for the next substep: as in configuration 29
+    // reads of slot i for the next substep: X[a] (a < FN - 1) at slots
+    // FM (a + 1) and FM (a + 1) + 1, the last X at x7 and x7 + 1, Y[b] at
+    // y0 + YS b
     auto reads = [&](int i, int SR, int BR, int kr, half8 (&ynext)[FM], int y0, int x7) {
+        constexpr int YS = T::YS;
         if (i >= FM && i <= FM * (FN - 1) + 1 && (i % FM) < 2) read_xh(BR, kr, i / FM - 1, i % FM);
         if (i == x7 || i == x7 + 1) read_xh(BR, kr, FN - 1, i - x7);
-        if (i >= y0 && i < y0 + 4 * FM && ((i - y0) & 3) == 0) read_y(SR, kr, (i - y0) >> 2, ynext[(i - y0) >> 2]);
+        if (i >= y0 && i < y0 + YS * FM && ((i - y0) % YS) == 0) read_y(SR, kr, (i - y0) / YS, ynext[(i - y0) / YS]);
     };
     auto mma = [&](int i, int ks, const half8 (&ys)[FM]) {
         const int a = i / FM;
