@@ -60,11 +60,11 @@ enum gsr_activation {
 /* One compiled tile configuration.  A workgroup of waves_m*waves_n wave64s
  * owns a block_m x block_n tile of C and walks K in steps of block_k through
  * `stages` LDS buffers (0 or 1: two per operand; configurations 28, 29 and
- * 31: two for A, three for B); each wave owns a (block_m/waves_m) x
- * (block_n/waves_n) sub-tile (configuration 31 adds waves_m * waves_n waves
- * that only copy operands into LDS).  Configurations 25, 28, 29 and 31 build
- * that sub-tile from 16x16x32
- * fp16 MFMAs, all others from 32x32x16 fp16 MFMAs.  (The K-split kinds, block_k
+ * 31: two for A, three for B; 2 or more: a ring of that many buffers per
+ * operand); each wave owns a (block_m/waves_m) x (block_n/waves_n) sub-tile
+ * (configurations 31 and 32 add waves_m * waves_n waves that only copy
+ * operands into LDS).  Configurations 25, 28, 29, 31 and 32 build that
+ * sub-tile from 16x16x32 fp16 MFMAs, all others from 32x32x16 fp16 MFMAs.  (The K-split kinds, block_k
  * 128 with waves 1 x 1, give every wave the whole tile and a share of each
  * K-step instead.)  group_m is the number of tile rows in one group of the
  * grouped launch order; xcd_remap picks how workgroup ids map to tiles: 0 the

@@ -57,7 +57,7 @@ def test_config_table(native):
         # LDS buffers each; stages >= 2: ring of LDS buffers filled by copies
         buffers = 2 if c["stages"] in (0, 1) else c["stages"]
         lds = buffers * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
-        if i in (28, 29, 31, 32):  # two A buffers and three B buffers
+        if i in (28, 29, 31):  # two A buffers and three B buffers
             lds = (2 * c["block_m"] + 3 * c["block_n"]) * c["block_k"] * 2
         assert c["lds_bytes"] == lds <= 163840
     for bad in (-1, max(ids) + 1) + RETIRED_IDS:

@@ -151,9 +151,11 @@ def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
 # order, so they give the same bits: the 256x256 kernel with B copied to LDS
 # (config 28) and its register-transpose twin (config 25); the 128x256
 # kernel with its copies on separate waves (config 31) and the same plan with
-# the copies among the MFMAs (config 29).  K covers 1 to 65 steps of 64, M
-# and N ragged against the tile, the element path included (N or K odd).
-@pytest.mark.parametrize("pair", [(28, 25), (31, 29)], ids=lambda p: f"{p[0]}vs{p[1]}")
+# the copies among the MFMAs (config 29); the 128x128 copy-wave kernel with a
+# four-stage ring (config 32) and config 31, whose tiles differ but whose
+# MFMA chains per output do not.  K covers 1 to 65 steps of 64, M and N
+# ragged against the tile, the element path included (N or K odd).
+@pytest.mark.parametrize("pair", [(28, 25), (31, 29), (32, 31)], ids=lambda p: f"{p[0]}vs{p[1]}")
 @pytest.mark.parametrize("shape", [(256, 256, 8), (300, 520, 200), (257, 1031, 72), (1000, 1500, 704),
                                    (513, 777, 4160), (4097, 2048, 1000), (2048, 4096, 1031)],
                          ids=lambda s: "x".join(map(str, s)))

@@ -20,10 +20,11 @@ and check them:
   checks each fragment against the 16x16x32 operand layout, with both
   operands pairing the same k, and that the eight rows the LDS serves per
   cycle sit on distinct banks;
-* for configuration 31 (gsr_interleave16c.hpp), whose copies run on waves of
-  their own, a barrier-interval model of the two roles: every stage the MFMA
-  waves read in an interval has landed by the barrier that opens it, and no
-  copy writes a stage during an interval in which it is read.
+* for the copy-wave kernels (gsr_interleave16c.hpp: two A and three B
+  stages, or one ring of A+B stages), a barrier-interval model of the two
+  roles: every stage the MFMA waves read in an interval has landed by the
+  barrier that opens it, and no copy writes a stage during an interval in
+  which it is read.
 
 Planted mistakes in the plan (a copy before the barrier, an operand read too
 late) are caught by the model, so it is not vacuous.
@@ -42,7 +43,7 @@ HDR_C = os.path.join(CSRC, "gsr_interleave16c.hpp")
 TILES = {"Ilv16DCfg": (256, 256), "Ilv16HDCfg": (128, 256)}
 COPY_WAVE_TILES = {"Ilv16CCfg": (128, 256), "Ilv16QCCfg": (128, 128)}
 SLOT_KEYS = ("X7_0", "X7_1", "Y0_0", "Y0_1", "BAR", "BC0", "BCD", "AC0", "ACD")
-COPY_WAVE_KEYS = ("X7_0", "X7_1", "Y0_0", "Y0_1", "YS", "BAR")
+COPY_WAVE_KEYS = ("X7_0", "X7_1", "Y0_0", "Y0_1", "YS", "BAR", "RING")
 
 
 def _constants(header: str, struct: str, keys) -> dict:
@@ -68,14 +69,15 @@ def plan(struct: str) -> dict:
     """The slot constants of one tile configuration, read from the header.
     For the copy-wave kernels the copies are placed where the copy waves
     issue them relative to the barriers: B(t+2) before any read of substep 0
-    (right after b_{t-1}), A(t+2) right after b_t."""
+    (right after b_{t-1}), A(t+2) right after b_t; with a ring of RING
+    stages, both copies of step t+RING right after b_t."""
     if struct in COPY_WAVE_TILES:
         c = _constants(HDR_C, struct, COPY_WAVE_KEYS)
         bm, bn = COPY_WAVE_TILES[struct]
         c.update(BC0=0, BCD=1, AC0=c["BAR"], ACD=1)
     else:
         c = _constants(HDR, struct, SLOT_KEYS)
-        c["YS"] = 4
+        c.update(YS=4, RING=0)
         bm, bn = TILES[struct]
     c["FM"], c["FN"] = bm // 2 // 16, bn // 2 // 16
     c["A_PER"], c["B_PER"] = bm * 64 * 2 // 1024 // 4, bn * 64 * 2 // 1024 // 4
@@ -86,13 +88,16 @@ def plan(struct: str) -> dict:
 
 def program(c: dict, ksteps: int) -> list:
     """The kernel's issue order: prologue, then per K-step t (A stage t % 2,
-    B stage t % 3) substep 0 and substep 1, slot by slot, as the loops in
-    gsr_interleave16d.hpp emit them."""
-    FM, FN = c["FM"], c["FN"]
+    B stage t % 3; with a ring, both t % RING) substep 0 and substep 1, slot
+    by slot, as the loops in gsr_interleave16d.hpp and gsr_interleave16c.hpp
+    emit them."""
+    FM, FN, ring = c["FM"], c["FN"], c["RING"]
+    per = c["A_PER"] + c["B_PER"]
     slots = FM * FN
-    ev = [("copyA", 0, 0)] * c["A_PER"] + [("copyB", 0, 0)] * c["B_PER"]
-    ev += [("copyA", 1, 1)] * c["A_PER"] + [("copyB", 1, 1)] * c["B_PER"]
-    ev += [("wait", c["A_PER"] + c["B_PER"]), ("barrier",)]
+    ev = []
+    for s in range(ring or 2):
+        ev += [("copyA", s, s)] * c["A_PER"] + [("copyB", s, s)] * c["B_PER"]
+    ev += [("wait", (ring - 1) * per if ring else per), ("barrier",)]
     for a in range(FN):
         ev += [("readX", a, 0, 0, 0, 0), ("readX", a, 1, 0, 0, 0)]
     ev += [("readY", b, 0, 0, 0) for b in range(FM)]
@@ -106,19 +111,22 @@ def program(c: dict, ksteps: int) -> list:
             ev.append(("readY", (i - y0) // c["YS"], sr, t, kr))
 
     for t in range(ksteps):
-        sa, sb = t % 2, t % 3
+        sa, sb = (t % ring, t % ring) if ring else (t % 2, t % 3)
+        san, sbn = ((t + 1) % ring, (t + 1) % ring) if ring else (sa ^ 1, (sb + 1) % 3)
         for i in range(slots):
             ev.append(("mma", i, t, 0))
             reads(i, sa, sb, t, 1, c["Y0_0"], c["X7_0"])
-            if i >= c["BC0"] and (i - c["BC0"]) % c["BCD"] == 0 and (i - c["BC0"]) // c["BCD"] < c["B_PER"]:
+            if not ring and i >= c["BC0"] and (i - c["BC0"]) % c["BCD"] == 0 and (i - c["BC0"]) // c["BCD"] < c["B_PER"]:
                 ev.append(("copyB", (t + 2) % 3, t + 2))
         for i in range(slots):
             ev.append(("mma", i, t, 1))
             if i == c["BAR"]:
-                ev += [("wait", c["B_PER"]), ("barrier",)]
+                ev += [("wait", (ring - 2) * per if ring else c["B_PER"]), ("barrier",)]
+                if ring:
+                    ev += [("copyA", sa, t + ring)] * c["A_PER"] + [("copyB", sb, t + ring)] * c["B_PER"]
             if i >= c["BAR"]:
-                reads(i, sa ^ 1, (sb + 1) % 3, t + 1, 0, c["Y0_1"], c["X7_1"])
-            if i >= c["AC0"] and (i - c["AC0"]) % c["ACD"] == 0 and (i - c["AC0"]) // c["ACD"] < c["A_PER"]:
+                reads(i, san, sbn, t + 1, 0, c["Y0_1"], c["X7_1"])
+            if not ring and i >= c["AC0"] and (i - c["AC0"]) % c["ACD"] == 0 and (i - c["AC0"]) // c["ACD"] < c["A_PER"]:
                 ev.append(("copyA", sa, t + 2))
     return ev
 
@@ -126,8 +134,9 @@ def program(c: dict, ksteps: int) -> list:
 def check_program(c: dict, ksteps: int) -> None:
     FM, FN = c["FM"], c["FN"]
     ev = program(c, ksteps)
-    assert sum(e[0] == "copyB" for e in ev) == c["B_PER"] * (ksteps + 2), "every B copy issued once"
-    assert sum(e[0] == "copyA" for e in ev) == c["A_PER"] * (ksteps + 2), "every A copy issued once"
+    ahead = c["RING"] or 2  # copies issued past the last K-step (they write zeros)
+    assert sum(e[0] == "copyB" for e in ev) == c["B_PER"] * (ksteps + ahead), "every B copy issued once"
+    assert sum(e[0] == "copyA" for e in ev) == c["A_PER"] * (ksteps + ahead), "every A copy issued once"
     X, half, X7, Y = {}, {}, {}, {}
     in_flight, landed = [], {"A": {}, "B": {}}
     published, last_read = {"A": {}, "B": {}}, {"A": {}, "B": {}}
@@ -169,8 +178,12 @@ def check_program(c: dict, ksteps: int) -> None:
             assert Y.get((ks, b)) == (t, ks), f"MFMA slot {i} of step {t} substep {ks} sees A^T fragment {Y.get((ks, b))}"
 
 
-@pytest.mark.parametrize("struct", sorted(TILES) + sorted(COPY_WAVE_TILES))
-@pytest.mark.parametrize("ksteps", [2, 4, 6, 8, 14])
+def _step_counts(struct):
+    """The two-plus-three layout runs K-steps in pairs, a ring one by one."""
+    return [1, 2, 3, 4, 5, 6, 7, 8, 14] if plan(struct)["RING"] else [2, 4, 6, 8, 14]
+
+
+@pytest.mark.parametrize("struct,ksteps", [(s, k) for s in sorted(TILES) + sorted(COPY_WAVE_TILES) for k in _step_counts(s)])
 def test_slot_plan_is_consistent(struct, ksteps):
     check_program(plan(struct), ksteps)
 
@@ -274,37 +287,58 @@ def test_copy_and_read_addresses(tile):
     assert extra_bank_cycles == 0
 
 
-# ---- the copy-wave protocol (configuration 31, gsr_interleave16c.hpp) -----------
+# ---- the copy-wave protocol (gsr_interleave16c.hpp) --------------------------
 
-def copy_wave_program(ksteps: int, a_before_barrier: bool = False, wait=8) -> list:
-    """Copy waves' issue order: stage 0 and 1 copies, wait, prologue barrier;
-    per K-step t the B(t+2) copies, the wait, barrier b_t and the A(t+2)
-    copies; then a full drain and the epilogue's barrier."""
-    ev = [("copy", "A", 0, 0)] * 4 + [("copy", "B", 0, 0)] * 8 + [("copy", "A", 1, 1)] * 4 + [("copy", "B", 1, 1)] * 8
-    ev += [("wait", 12), ("barrier",)]
-    for t in range(ksteps):
-        ev += [("copy", "B", (t + 2) % 3, t + 2)] * 8
-        if a_before_barrier:
-            ev += [("copy", "A", t % 2, t + 2)] * 4
-        ev += [("wait", wait), ("barrier",)]
-        if not a_before_barrier:
-            ev += [("copy", "A", t % 2, t + 2)] * 4
+def copy_wave_program(ksteps: int, ring: int = 0, a_per: int = 4, b_per: int = 8,
+                      a_before_barrier: bool = False, wait=None) -> list:
+    """Copy waves' issue order.  Two A and three B stages (ring 0): stage 0
+    and 1 copies, wait, prologue barrier; per K-step t the B(t+2) copies, the
+    wait, barrier b_t and the A(t+2) copies.  A ring of `ring` stages: the
+    copies of steps 0 .. ring-1, wait, prologue barrier; per K-step t the
+    wait, b_t and the copies of step t+ring into stage t mod ring.  Both end
+    with a full drain and the epilogue's barrier."""
+    per = a_per + b_per
+    ev = []
+    if not ring:
+        ev += [("copy", "A", 0, 0)] * a_per + [("copy", "B", 0, 0)] * b_per
+        ev += [("copy", "A", 1, 1)] * a_per + [("copy", "B", 1, 1)] * b_per
+        ev += [("wait", per), ("barrier",)]
+        for t in range(ksteps):
+            ev += [("copy", "B", (t + 2) % 3, t + 2)] * b_per
+            if a_before_barrier:
+                ev += [("copy", "A", t % 2, t + 2)] * a_per
+            ev += [("wait", b_per if wait is None else wait), ("barrier",)]
+            if not a_before_barrier:
+                ev += [("copy", "A", t % 2, t + 2)] * a_per
+    else:
+        for st in range(ring):
+            ev += [("copy", "A", st, st)] * a_per + [("copy", "B", st, st)] * b_per
+        ev += [("wait", (ring - 1) * per), ("barrier",)]
+        for t in range(ksteps):
+            copies = [("copy", "A", t % ring, t + ring)] * a_per + [("copy", "B", t % ring, t + ring)] * b_per
+            if a_before_barrier:
+                ev += copies
+            ev += [("wait", (ring - 2) * per if wait is None else wait), ("barrier",)]
+            if not a_before_barrier:
+                ev += copies
     return ev + [("wait", 0), ("barrier",)]
 
 
-def mfma_wave_reads(ksteps: int) -> list:
+def mfma_wave_reads(ksteps: int, ring: int = 0) -> list:
     """MFMA waves' stage reads per barrier interval: (interval, operand,
     stage, K-step of the data).  Interval j follows the j-th barrier of the
     kernel (the prologue's is the first, b_t the (t+2)-th)."""
+    sa = (lambda t: t % ring) if ring else (lambda t: t % 2)
+    sb = (lambda t: t % ring) if ring else (lambda t: t % 3)
     reads = [(1, "A", 0, 0), (1, "B", 0, 0)]  # step 0's substep-0 operands
     for t in range(ksteps):
-        reads += [(t + 1, "A", t % 2, t), (t + 1, "B", t % 3, t)]                    # substep 0, for substep 1
-        reads += [(t + 2, "A", (t + 1) % 2, t + 1), (t + 2, "B", (t + 1) % 3, t + 1)]  # after b_t
+        reads += [(t + 1, "A", sa(t), t), (t + 1, "B", sb(t), t)]                  # substep 0, for substep 1
+        reads += [(t + 2, "A", sa(t + 1), t + 1), (t + 2, "B", sb(t + 1), t + 1)]  # after b_t
     return reads
 
 
-def check_copy_waves(ksteps: int, **kw) -> None:
-    ev = copy_wave_program(ksteps, **kw)
+def check_copy_waves(ksteps: int, ring: int = 0, **kw) -> None:
+    ev = copy_wave_program(ksteps, ring=ring, **kw)
     interval, in_flight = 0, []
     landed = {}           # (operand, stage) -> K-step whose copies have landed
     landed_at = {}        # barrier index -> snapshot of landed data at that barrier
@@ -322,18 +356,34 @@ def check_copy_waves(ksteps: int, **kw) -> None:
             interval += 1
             landed_at[interval] = dict(landed)
     assert interval == ksteps + 2, "copy and MFMA waves pass the same number of barriers"
-    for j, op, st, step in mfma_wave_reads(ksteps):
+    for j, op, st, step in mfma_wave_reads(ksteps, ring):
         assert landed_at[j].get((op, st)) == step, f"{op} stage {st} read in interval {j} before step {step} landed"
         assert (op, st) not in written_in.get(j, set()), f"{op} stage {st} copied into while it is read (interval {j})"
 
 
-@pytest.mark.parametrize("ksteps", [2, 4, 6, 8, 14])
-def test_copy_wave_protocol(ksteps):
-    check_copy_waves(ksteps)
+def copy_wave_geometry(struct: str) -> dict:
+    c = plan(struct)
+    return {"ring": c["RING"], "a_per": c["A_PER"], "b_per": c["B_PER"]}
 
 
-@pytest.mark.parametrize("mistake", [{"a_before_barrier": True}, {"wait": 12}],
-                         ids=["A-copies-before-the-barrier", "wait-too-loose"])
-def test_copy_wave_model_catches_planted_mistakes(mistake):
+@pytest.mark.parametrize("struct,ksteps", [(s, k) for s in sorted(COPY_WAVE_TILES) for k in _step_counts(s)])
+def test_copy_wave_protocol(struct, ksteps):
+    check_copy_waves(ksteps, **copy_wave_geometry(struct))
+
+
+@pytest.mark.parametrize("struct", sorted(COPY_WAVE_TILES))
+@pytest.mark.parametrize("mistake", ["A-copies-before-the-barrier", "wait-too-loose"])
+def test_copy_wave_model_catches_planted_mistakes(struct, mistake):
+    g = copy_wave_geometry(struct)
+    per = g["a_per"] + g["b_per"]
+    if mistake == "A-copies-before-the-barrier":
+        kw = {"a_before_barrier": True}
+    else:  # one step more in flight than the barrier allows
+        kw = {"wait": (g["ring"] - 1) * per if g["ring"] else per}
     with pytest.raises(AssertionError):
-        check_copy_waves(8, **mistake)
+        check_copy_waves(8, **g, **kw)
+
+
+def test_ring_depth_is_read_from_the_header():
+    assert copy_wave_geometry("Ilv16CCfg")["ring"] == 0
+    assert copy_wave_geometry("Ilv16QCCfg")["ring"] >= 3

@@ -124,12 +124,13 @@ struct Entry {
             launch_kspec<BM, BN, S, D>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64                \
     }
 
-// An explicitly interleaved kernel (stages = 1: two LDS buffers per operand);
+// An explicitly interleaved kernel (stages 1: two LDS buffers per operand, or
+// two for A and three for B; stages >= 2: a ring of that many A+B buffers);
 // its element-wise path is the register-staged kernel of the same tile.
-#define GSR_ILV(ID, BM, BN, LDS, FN, XCD)                                                              \
-    Entry                                                                                             \
-    {                                                                                                 \
-        {ID, BM, BN, 64, 2, 2, 1, 4, XCD, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN     \
+#define GSR_ILV(ID, BM, BN, STAGES, LDS, FN, XCD)                                                          \
+    Entry                                                                                                 \
+    {                                                                                                     \
+        {ID, BM, BN, 64, 2, 2, STAGES, 4, XCD, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN    \
     }
 
 // The compiled tile table, by id.  Ids are stable from one library version to
@@ -154,19 +155,19 @@ const Entry kTable[] = {
     // 256x256 on the 16x16x32 MFMA (8 x 8 blocks of 16x16 per wave), B transposed through
     // registers: configuration 28's twin (same bits), kept for comparison; chip rounds of
     // 16 x 16 tiles where the grid divides into them
-    GSR_ILV(25, 256, 256, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16, 2),
+    GSR_ILV(25, 256, 256, 1, gsr::Ilv16Cfg::LDS_BYTES, launch_ilv16, 2),
     // configuration 25 with B copied to LDS as stored and read with transpose reads: the
     // selector's 256x256 tile
-    GSR_ILV(28, 256, 256, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16DCfg>, 2),
+    GSR_ILV(28, 256, 256, 1, gsr::Ilv16DCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16DCfg>, 2),
     // configuration 28's kernel on the 128x256 tile (8 x 4 blocks of 16x16 per wave):
     // configuration 31's twin (same bits), kept for comparison
-    GSR_ILV(29, 128, 256, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
+    GSR_ILV(29, 128, 256, 1, gsr::Ilv16HDCfg::LDS_BYTES, launch_ilv16d<gsr::Ilv16HDCfg>, 1),
     // configuration 29 with its copies issued by four extra copy waves (512 threads): the
     // selector's 128x256 tile
-    GSR_ILV(31, 128, 256, gsr::Ilv16CCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16CCfg>, 1),
-    // the same kernel on the 128x128 tile (B rows of 256 bytes, 4 x 4 blocks per MFMA wave):
-    // the selector's 128x128 tile
-    GSR_ILV(32, 128, 128, gsr::Ilv16QCCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16QCCfg>, 1),
+    GSR_ILV(31, 128, 256, 1, gsr::Ilv16CCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16CCfg>, 1),
+    // the same kernel on the 128x128 tile (B rows of 256 bytes, 4 x 4 blocks per MFMA wave)
+    // with one ring of four A+B stages: the selector's 128x128 tile
+    GSR_ILV(32, 128, 128, gsr::Ilv16QCCfg::RING, gsr::Ilv16QCCfg::LDS_BYTES, launch_ilv16c<gsr::Ilv16QCCfg>, 1),
 };
 constexpr int kNumConfigs = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -183,7 +184,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile selection.  A candidate's cost is the time of one tile,
 //     2 * bm * bn * K / (per-CU rate) + per-tile overhead,
 // times its waves of workgroups on 256 CUs, where a last wave that is not
-// full costs max(0.60, 0.55 + 0.45 * fill) of a full one (a part-filled chip
+// full costs max(0.80, 0.35 + 0.65 * fill) of a full one (a part-filled chip
 // runs at a higher power-limited clock, but every tile still pays its fixed
 // cost).  The 256x256, 128x256 and 128x128 tiles have one candidate each, the
 // 16x16x32 kernels with B copied to LDS (configuration 28, and configurations
@@ -197,7 +198,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // benchmark workloads), the offline sweep the aikraft.ru guide describes in
 // sections 3 and 7 (tiled_dense_gemm_scale_amd/fit_selector.py on
 // tuning/mi355x_config_times.csv reproduces this table); on those shapes the
-// choice is on average within 0.12 % of the fastest configuration, 4.3 % at
+// choice is on average within 0.08 % of the fastest configuration, 2.7 % at
 // worst.  Below K = 256 the four-wave K-split tiles replace their copy-wave
 // twins (at two K-steps the copy waves have nothing to run ahead of).
 struct Candidate {
@@ -206,18 +207,18 @@ struct Candidate {
     double tile_us;        // fixed cost per tile: prologue, epilogue, stores
 };
 const Candidate kCandidates[] = {
-    {28, 5.821, 13.108},  // 256x256, 16x16x32, B copied to LDS
-    {31, 5.759, 8.723},   // 128x256, 16x16x32, B copied to LDS by copy waves
-    {32, 3.733, 4.850},   // 128x128, 16x16x32, B copied to LDS by copy waves
-    {5, 3.735, 12.205},   // 256x128
-    {10, 1.996, 6.495},   // 64x128
-    {8, 2.377, 6.225},    // 128x64
-    {21, 2.786, 3.654},   // 64x64, K split, copy waves       (K > 256)
-    {22, 1.834, 2.719},   // 32x64, K split, copy waves       (K > 256)
-    {16, 2.513, 4.233},   // 64x64, K split, four waves       (K <= 256)
-    {18, 1.673, 3.293},   // 32x64, K split, four waves       (K <= 256)
+    {28, 6.472, 8.592},   // 256x256, 16x16x32, B copied to LDS
+    {31, 6.221, 5.891},   // 128x256, 16x16x32, B copied to LDS by copy waves
+    {32, 5.198, 4.377},   // 128x128, 16x16x32, A and B copied to LDS by copy waves
+    {5, 3.868, 7.926},    // 256x128
+    {10, 1.963, 4.632},   // 64x128
+    {8, 2.303, 4.543},    // 128x64
+    {21, 2.751, 3.364},   // 64x64, K split, copy waves       (K > 256)
+    {22, 1.804, 2.500},   // 32x64, K split, copy waves       (K > 256)
+    {16, 2.453, 3.763},   // 64x64, K split, four waves       (K <= 256)
+    {18, 1.645, 2.987},   // 32x64, K split, four waves       (K <= 256)
 };
-constexpr double kPartMin = 0.60, kPartA = 0.55;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
+constexpr double kPartMin = 0.80, kPartA = 0.35;  // a part-filled last wave: max(kPartMin, kPartA + (1 - kPartA) * fill)
 
 int select(int64_t M, int64_t N, int64_t K)
 {
@@ -340,7 +341,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 720; }
+int gsr_version(void) { return 730; }
 
 const char* gsr_status_string(int status)
 {

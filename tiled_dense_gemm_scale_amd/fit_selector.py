@@ -6,9 +6,9 @@ The selector in csrc/gsr_api.hip prices a candidate tile bm x bn as
 
 with wgs = ceil(M / bm) * ceil(N / bn) workgroups on 256 CUs and
 waves(wgs) = full waves + (a part-filled last wave: max(pmin, a + (1 - a) * fill)).
-The 256x256 and 128x256 tiles have one kernel each, the 16x16x32 kernels with
-B copied to LDS (configs 28 and 29): each was measured faster than every other
-kernel of its tile on every one of the 60 shapes.  This module fits `rate`
+The 256x256, 128x256 and 128x128 tiles have one kernel each, the 16x16x32
+kernels with B copied to LDS (configs 28, 31 and 32): each was measured faster
+than every other kernel of its tile on every one of the 60 shapes.  This module fits `rate`
 (TFLOP/s per CU) and `tile_us` per configuration by least squares in relative
 error, and picks (a, pmin) on a grid whose choices come closest to the
 fastest measured configuration (mean log ratio).  Input: the CSV written from
