@@ -126,12 +126,14 @@ def test_ragged_every_config(gsr, orc, shape):
 
 # K-split tiles with separate copy waves against the four-wave K-split kernel
 # of the same tile: same K split, same summation order, so the same bits.
-# K covers 1, 2, 3, 4 and 9 steps of 128; M and N ragged against the tile.
+# K covers 1, 2, 3, 4, 8, 9 and 32 steps of 128; M and N ragged against the
+# tile (M of 1, 5, 16, 33 and 40 against 32- and 64-row tiles).
 COPY_WAVE_TWINS = [(21, 16), (22, 18)]
 
 
 @pytest.mark.parametrize("shape", [(64, 64, 8), (100, 72, 136), (1024, 1024, 264), (33, 200, 392),
-                                   (520, 1000, 1032), (16, 11008, 4096)], ids=lambda s: "x".join(map(str, s)))
+                                   (520, 1000, 1032), (16, 11008, 4096), (1, 4096, 1000), (5, 300, 777),
+                                   (40, 520, 2000)], ids=lambda s: "x".join(map(str, s)))
 def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
     M, N, K = shape
     a, b = W.normal_inputs(M, N, K, seed=M + 3 * N + 5 * K)
