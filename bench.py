@@ -496,15 +496,41 @@ def main(argv=None) -> int:
                 warm.append((e0, e1))
         torch.cuda.synchronize()
         warm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in warm)[len(warm) // 2]
-        del flush, clean, sink
+        # a reference from the same two states: a device-to-device copy of B
+        # (its bytes read once and written once), timed the same way, so the
+        # call's cold rate can be set beside what a plain stream of B reaches
+        bcopy = torch.empty_like(b)
+        ref = {"cold": [], "warm": []}
+        with torch.cuda.stream(stream):
+            for state in ("cold", "warm"):
+                for i in range(len(cold)):
+                    if state == "cold":
+                        flush.fill_(float(i))
+                        sink.copy_(clean.view(-1, 32)[:, 0])
+                    else:
+                        sink[:4096].fill_(float(i))
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    bcopy.copy_(b)
+                    e1.record(stream)
+                    ref[state].append((e0, e1))
+        torch.cuda.synchronize()
+        copy_ms = {k: sorted(e0.elapsed_time(e1) for e0, e1 in v)[len(v) // 2] for k, v in ref.items()}
+        del flush, clean, sink, bcopy
         torch.cuda.empty_cache()
         context["cold_us_per_call"] = round(cold_ms * 1e3, 3)
         context["cold_tflops"] = round(w.flops / (cold_ms * 1e-3) / 1e12, 3)
         context["warm_single_call_us"] = round(warm_ms * 1e3, 3)
         if w.flops / w.algorithmic_bytes < PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
             context["cold_hbm_gbs_algorithmic"] = round(w.algorithmic_bytes / (cold_ms * 1e-3) / 1e9, 1)
+        b_bytes = b.numel() * b.element_size()
+        context["cold_copy_of_b_us"] = round(copy_ms["cold"] * 1e3, 3)
+        context["warm_copy_of_b_us"] = round(copy_ms["warm"] * 1e3, 3)
+        context["cold_copy_of_b_gbs_read_plus_write"] = round(2 * b_bytes / (copy_ms["cold"] * 1e-3) / 1e9, 1)
         log(f"[bench] cold caches (median of {len(cold)}): {cold_ms * 1e3:.2f} us/call "
-            f"({context['cold_tflops']} TFLOP/s); warm single calls {warm_ms * 1e3:.2f} us/call")
+            f"({context['cold_tflops']} TFLOP/s); warm single calls {warm_ms * 1e3:.2f} us/call; "
+            f"a copy of B ({b_bytes / 1e6:.1f} MB): {copy_ms['cold'] * 1e3:.2f} us cold, {copy_ms['warm'] * 1e3:.2f} us warm")
     if graph is not None and args.zero_input:
         za = torch.zeros_like(a)
         zb = torch.zeros_like(b)
