@@ -39,7 +39,7 @@ def test_config_struct_layout(native):
 
 
 # Ids of configurations dropped from the table; they are never reused.
-RETIRED_IDS = (0, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14, 15, 19, 20, 23, 24, 26)
+RETIRED_IDS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 19, 20, 23, 24, 26)
 
 
 def test_config_table(native):
@@ -179,22 +179,22 @@ def test_tuning_table_host_side(native, tmp_path):
     base = native.select_config(1024, 1024, 1024)
     other = native.select_config(1024, 1024, 1025)
     good = tmp_path / "t.txt"
-    good.write_text("# comment line\n\n1024 1024 1024 8 2 0   # trailing comment\n300 520 200 28 8 1\n")
+    good.write_text("# comment line\n\n1024 1024 1024 22 2 0   # trailing comment\n300 520 200 28 8 1\n")
     native.load_tuning(str(good))
     try:
         assert native.tuning_entries() == 2
         c = native.select_config(1024, 1024, 1024)
-        assert (c["id"], c["group_m"], c["xcd_remap"]) == (8, 2, 0)
+        assert (c["id"], c["group_m"], c["xcd_remap"]) == (22, 2, 0)
         c = native.select_config(300, 520, 200)
         assert (c["id"], c["group_m"], c["xcd_remap"]) == (28, 8, 1)
         assert native.select_config(1024, 1024, 1025) == other  # not in the table
         for bad in ("1024 1024 1024 99 1 0\n",      # unknown config id
                     "1024 1024 1024 9 1 0\n",       # a retired config id
-                    "1024 1024 1024 7 0 0\n",       # group_m < 1
-                    "1024 1024 1024 7 1 3\n",       # xcd_remap not 0, 1 or 2
-                    "1024 1024 7 1 0\n",            # too few fields
-                    "1024 1024 1024 7 1 0 5\n",     # too many fields
-                    "-1 4 4 7 1 0\n",               # negative size
+                    "1024 1024 1024 21 0 0\n",      # group_m < 1
+                    "1024 1024 1024 21 1 3\n",      # xcd_remap not 0, 1 or 2
+                    "1024 1024 21 1 0\n",           # too few fields
+                    "1024 1024 1024 21 1 0 5\n",    # too many fields
+                    "-1 4 4 21 1 0\n",              # negative size
                     "hello\n"):
             p = tmp_path / "bad.txt"
             p.write_text(bad)
@@ -211,7 +211,7 @@ def test_tuning_table_host_side(native, tmp_path):
 
 def test_launch_entry_point_checks(native):
     # explicit launches are validated on the host before any device work
-    for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (8, 0, 1), (8, 5000, 1), (8, 4, 3), (8, 4, -1), (9, 4, 1), (7, 4, 1), (23, 4, 1)):
+    for cid, gm, xcd in ((99, 4, 1), (-1, 4, 1), (21, 0, 1), (21, 5000, 1), (21, 4, 3), (21, 4, -1), (9, 4, 1), (7, 4, 1), (23, 4, 1), (8, 4, 1)):
         st = native.gemm_scale_bias_act_cfg(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 0, 0, cid, gm, xcd)
         assert st == 6, (cid, gm, xcd, st)
 

@@ -226,7 +226,7 @@ def test_empty_outputs(gsr):
     assert gsr.gemm_scale_relu(a2, b2, 0.5).shape == (4, 0)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 17, 18, 21, 22, 25, 28, 29, 31, 32])
+@pytest.mark.parametrize("cid", [-1, 16, 17, 18, 21, 22, 25, 28, 29, 31, 32])
 def test_c_aligned_to_8_not_16_bytes(gsr, orc, cid):
     """A and B 16-byte aligned, C only 8-byte aligned (4 elements into a 16-byte
     aligned buffer): the 128-bit stores need 16-byte aligned rows of C, so
@@ -266,7 +266,7 @@ def test_unaligned_pointers(gsr, orc, offset):
     PT.assert_parity(f"unaligned+{offset}", bits(cd.cpu()), ref)
 
 
-@pytest.mark.parametrize("cid", [-1, 5, 21, 25, 28, 29, 31, 32])
+@pytest.mark.parametrize("cid", [-1, 21, 22, 25, 28, 29, 31, 32])
 def test_guard_bands_and_full_coverage(gsr, orc, cid):
     """C sits inside a larger buffer filled with a sentinel: the bands before
     and after stay untouched and every element of C is written."""

@@ -88,7 +88,7 @@ def test_concurrent_host_threads(gsr, tmp_path):
         want.append(gsr.gemm_scale_bias_act(a, b, bias if i % 2 else None, 0.5, acts[i % 3]).clone())
     torch.cuda.synchronize()
     table = tmp_path / "t.txt"
-    table.write_text("".join(f"{M} {N} {K} 8 2 0\n" for (M, N, K) in shapes[:2]))
+    table.write_text("".join(f"{M} {N} {K} 21 2 0\n" for (M, N, K) in shapes[:2]))
     errors = []
     stop = threading.Event()
 

@@ -24,7 +24,7 @@ def gsr(native):
     g.clear_tuning()
 
 
-@pytest.mark.parametrize("cid,shape", [(28, (4097, 700, 264)), (16, (700, 1100, 264)), (8, (700, 1100, 264)),
+@pytest.mark.parametrize("cid,shape", [(28, (4097, 700, 264)), (16, (700, 1100, 264)), (17, (700, 1100, 264)),
                                        (18, (700, 1100, 264)), (21, (700, 1100, 264)), (22, (700, 1100, 264)),
                                        (25, (700, 1100, 264)), (29, (700, 1100, 264)),
                                        (25, (4096, 4096, 136)), (25, (8192, 4096, 72)), (28, (4096, 8192, 72)),
@@ -56,7 +56,7 @@ def test_tuning_table_steers_the_plain_call(gsr, tmp_path):
     a, b = W.normal_inputs(M, N, K, seed=3)
     ad, bd = a.to(DEV), b.to(DEV)
     sel = gsr.select_config(M, N, K)["id"]
-    forced = 8 if sel != 8 else 10
+    forced = 21 if sel != 21 else 22
     want = gsr.gemm_scale_relu_ex(ad, bd, 0.5, forced).clone()
     p = tmp_path / "tuning.txt"
     p.write_text(f"{M} {N} {K} {forced} 2 0\n")

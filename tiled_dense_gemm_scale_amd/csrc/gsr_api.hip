@@ -50,13 +50,6 @@ hipError_t launch_staged(const Problem& p, int grid, hipStream_t s)
                          dim3(gsr::kWave * WM * WN), s, p);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S>
-hipError_t launch_pipe(const Problem& p, int grid, hipStream_t s)
-{
-    return launch_kernel((gsr::gemm_scale_relu_pipe_kernel<BM, BN, BK, WM, WN, S>), dim3(grid),
-                         dim3(gsr::kWave * WM * WN), s, p);
-}
-
 hipError_t launch_ilv16(const Problem& p, int grid, hipStream_t s)
 {
     return launch_kernel(gsr::gemm_scale_relu_ilv16_kernel, dim3(grid), dim3(gsr::Ilv16Cfg::NT), s, p);
@@ -96,15 +89,6 @@ struct Entry {
     int elem_bm, elem_bn;  // the output tile of the element-wise kernel (its grid)
 };
 
-// Pipelined kernel: LDS ring of S stages filled by direct-to-LDS copies.  The
-// element-wise path of the same tile is the register-staged kernel.
-#define GSR_PIPE(ID, BM, BN, BK, WM, WN, S, GROUP)                                                    \
-    Entry                                                                                             \
-    {                                                                                                 \
-        {ID, BM, BN, BK, WM, WN, S, GROUP, 1, gsr::PipeCfg<BM, BN, BK, WM, WN, S>::LDS_BYTES},       \
-            launch_pipe<BM, BN, BK, WM, WN, S>, launch_staged<BM, BN, 64, WM, WN, false>, BM, BN      \
-    }
-
 // Four waves splitting K inside the workgroup (block_k = 128 per step, waves
 // 1 x 1 over the output tile), LDS ring of S stages.  Element-wise path: the
 // 64x64 register-staged kernel.
@@ -135,17 +119,16 @@ struct Entry {
 
 // The compiled tile table, by id.  Ids are stable from one library version to
 // the next, so a tuning table written earlier keeps its meaning; the ids of
-// configurations that were dropped (0-4, 6, 7, 9, 11-15, 19, 20, 23, 24, 26:
-// tiles that neither the selector nor any measured tuning entry chose; 15, 23
-// and 24, the 256x256, 128x256 and 128x128 tiles on 32x32x16 MFMAs, were
-// slower than configurations 28, 29 and 32 on every measured shape; 26, the
-// 128x256 tile with B transposed through registers, is served by 29 and 31)
+// configurations that were dropped (0-15, 19, 20, 23, 24, 26: tiles that
+// neither the selector nor any measured tuning entry chose; 15, 23 and 24,
+// the 256x256, 128x256 and 128x128 tiles on 32x32x16 MFMAs, were slower than
+// configurations 28, 29 and 32 on every measured shape; 26, the 128x256 tile
+// with B transposed through registers, is served by 29 and 31; 5, 8 and 10,
+// the pipelined 256x128, 128x64 and 64x128 tiles, were the fastest on none of
+// the 60 fitting shapes, and the fit without them chooses as well)
 // are not reused and are rejected with GSR_ERROR_INVALID_CONFIG.  Tile choice
 // per shape class is made by select().
 const Entry kTable[] = {
-    GSR_PIPE(5, 256, 128, 64, 2, 2, 3, 4),   // 4 waves of 128x64, 3 x 48 KiB
-    GSR_PIPE(8, 128, 64, 64, 2, 2, 6, 4),    // 4 waves of 64x32, 6 x 24 KiB
-    GSR_PIPE(10, 64, 128, 64, 2, 2, 6, 4),   // 4 waves of 32x64
     GSR_KSPLIT(16, 64, 64, 4, 4),            // 4 waves split K, whole 64x64 tile each
     GSR_KSPLIT(17, 64, 32, 6, 4),
     GSR_KSPLIT(18, 32, 64, 6, 4),
@@ -210,9 +193,6 @@ const Candidate kCandidates[] = {
     {28, 6.472, 8.592},   // 256x256, 16x16x32, B copied to LDS
     {31, 6.221, 5.891},   // 128x256, 16x16x32, B copied to LDS by copy waves
     {32, 5.198, 4.377},   // 128x128, 16x16x32, A and B copied to LDS by copy waves
-    {5, 3.868, 7.926},    // 256x128
-    {10, 1.963, 4.632},   // 64x128
-    {8, 2.303, 4.543},    // 128x64
     {21, 2.751, 3.364},   // 64x64, K split, copy waves       (K > 256)
     {22, 1.804, 2.500},   // 32x64, K split, copy waves       (K > 256)
     {16, 2.453, 3.763},   // 64x64, K split, four waves       (K <= 256)
@@ -341,7 +321,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void* A, const void* B, cons
 
 extern "C" {
 
-int gsr_version(void) { return 730; }
+int gsr_version(void) { return 740; }
 
 const char* gsr_status_string(int status)
 {

@@ -35,7 +35,7 @@ CUS = 256
 Shape = Tuple[int, int, int]
 # the selector's candidates; the copy-wave K-split tiles only for K > 256,
 # their four-wave twins only for K <= 256
-BASE = [28, 31, 32, 5, 10, 8]
+BASE = [28, 31, 32]
 COPY_WAVE = [21, 22]
 FOUR_WAVE = [16, 18]
 ALL = BASE + COPY_WAVE + FOUR_WAVE
