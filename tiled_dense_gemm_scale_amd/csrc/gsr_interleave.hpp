@@ -13,9 +13,11 @@
 // registers one block per thread, transposed with byte permutes and written
 // K-contiguous, or in the kernels of gsr_interleave16d.hpp and
 // gsr_interleave16c.hpp copied into LDS as stored and read with transpose
-// reads (the latter with four more waves that only issue the copies).  Both operands are requested two
-// K-steps ahead through buffer descriptors that advance along K in SGPRs, so
-// the compiler adds no waits of its own; the vmcnt bookkeeping is explicit.
+// reads (the latter with four more waves that only issue the copies).  Both
+// operands are requested two K-steps ahead (three in the 128x128 tile, which
+// keeps a ring of four stages) through buffer descriptors that advance along
+// K in SGPRs, so the compiler adds no waits of its own; the vmcnt
+// bookkeeping is explicit.
 // One barrier per K-step publishes the next step's buffers and frees the
 // current ones.  The kernels on this design: 256x256, 128x256 and 128x128
 // tiles on 16x16x32 MFMAs (gsr_interleave16.hpp, gsr_interleave16d.hpp,
@@ -24,7 +26,8 @@
 // Ragged edges: rows of A past M and rows of B past K fall outside the
 // advancing descriptors (read as zero); B columns past N and A columns past K
 // get an out-of-range offset per lane; stores outside C are dropped.  K is
-// walked in an even number of steps: a step wholly past K multiplies zeros.
+// walked in an even number of steps (the 128x128 ring: one by one): a step
+// wholly past K multiplies zeros.
 #pragma once
 
 #include <type_traits>
