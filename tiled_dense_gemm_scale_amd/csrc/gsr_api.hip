@@ -67,9 +67,6 @@ hipError_t launch_ilv16c(const Problem& p, int grid, hipStream_t s)
     return launch_kernel(gsr::gemm_scale_relu_ilv16c_kernel<T>, dim3(grid), dim3(T::NT), s, p);
 }
 
-
-
-
 template <int BM, int BN, int S>
 hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
 {
