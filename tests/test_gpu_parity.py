@@ -156,10 +156,13 @@ def test_copy_wave_ksplit_matches_its_twin(gsr, orc, shape):
 # the copies among the MFMAs (config 29); the 128x128 copy-wave kernel with a
 # four-stage ring (config 32) and config 31, whose tiles differ but whose
 # MFMA chains per output do not.  K covers 1 to 65 steps of 64, M and N
-# ragged against the tile, the element path included (N or K odd).
+# ragged against the tile, the element path included (N or K odd); the last
+# three shapes run the 128-bit path with 3, 17 and 66 K-steps, so the ring
+# of four ends on a tail of 3, 1 and 2 steps.
 @pytest.mark.parametrize("pair", [(28, 25), (31, 29), (32, 31)], ids=lambda p: f"{p[0]}vs{p[1]}")
 @pytest.mark.parametrize("shape", [(256, 256, 8), (300, 520, 200), (257, 1031, 72), (1000, 1500, 704),
-                                   (513, 777, 4160), (4097, 2048, 1000), (2048, 4096, 1031)],
+                                   (513, 777, 4160), (4097, 2048, 1000), (2048, 4096, 1031),
+                                   (384, 1024, 192), (640, 768, 1088), (1024, 2048, 4224)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_copy_transpose_twin_matches_register_transpose(gsr, orc, shape, pair):
     M, N, K = shape
