@@ -74,6 +74,17 @@ def test_column_shard_full(gsr, orc):
     PT.assert_parity(w.name, got, ref)
 
 
+def test_mid_size_full(gsr, orc):
+    """A 1024-row batch against 4096 x 4096 weights (the 128 x 128 tile's
+    class), every output, in the selector's launch."""
+    w = W.MID
+    a, b = W.workload_inputs(w)
+    say(f"[gpu] {w.name} {w.M}x{w.N}x{w.K} alpha={w.alpha} selector")
+    got = PT.run_gpu(a, b, w.alpha)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), w.alpha)
+    PT.assert_parity(w.name, got, ref)
+
+
 @pytest.mark.parametrize("name", ["square_16384"])
 def test_workload_sampled(gsr, orc, name):
     w = W.WORKLOADS[name]

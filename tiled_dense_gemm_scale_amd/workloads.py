@@ -72,8 +72,13 @@ COLSHARD8 = Workload("llm_mlp_colshard8_4097x1376x4096", 4097, 1376, 4096, 1.0, 
                      "one GPU's column shard of the LLM-MLP up-projection split over 8 GPUs "
                      "(N = 11008/8), A ~ N(0,1), B ~ N(0,1/K), alpha=1.0")
 
+# A 1024-row batch against 4096x4096 weights: a mid-size grid (256 tiles of
+# 128x128, 64 of 256x256), the class the 128x128 tile serves.
+MID = Workload("mid_1024x4096x4096", 1024, 4096, 4096, 1.0, 4096 ** -0.5, False,
+               "a 1024-row batch against 4096x4096 weights, A ~ N(0,1), B ~ N(0,1/K), alpha=1.0")
+
 # Shapes timed and tested besides the five workloads above.
-EXTRA: Dict[str, Workload] = {w.name: w for w in [SKINNY, COLSHARD8]}
+EXTRA: Dict[str, Workload] = {w.name: w for w in [SKINNY, COLSHARD8, MID]}
 
 
 def by_name(name: str) -> Workload:
