@@ -117,6 +117,8 @@ RAGGED = [
     (513, 384, 1000),
     (129, 1031, 72),      # N % 8 != 0: element path
     (1000, 1500, 704),
+    (200, 262, 130),      # rows of 2N, 2K = 4 mod 8 bytes: element path, 4-byte loads
+    (96, 300, 100),       # rows of 2N, 2K = 8 mod 16 bytes: element path, 8-byte loads
 ]
 
 
@@ -259,10 +261,11 @@ def test_c_aligned_to_8_not_16_bytes(gsr, orc, cid):
     PT.assert_parity(f"C+8 bytes cfg{cid}", hb[4:4 + M * N].reshape(M, N), ref)
 
 
-@pytest.mark.parametrize("offset", [1, 3, 8])
+@pytest.mark.parametrize("offset", [1, 2, 3, 4, 8])
 def test_unaligned_pointers(gsr, orc, offset):
-    """Operands at 2-byte (but not 16-byte) aligned addresses take the
-    element-wise path and give the same results."""
+    """Operands at 2-, 4- or 8-byte (but not 16-byte) aligned addresses take
+    the element-wise path, whose loads narrow to the alignment (2-, 4- or
+    8-byte units), and give the same results."""
     M, N, K = 130, 136, 72
     a, b = W.normal_inputs(M, N, K, seed=offset)
     ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)

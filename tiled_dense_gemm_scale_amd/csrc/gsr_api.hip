@@ -290,6 +290,17 @@ int check_device()
     return GSR_SUCCESS;
 }
 
+// The element-wise kernel's load unit for an operand whose rows are `len`
+// fp16 values long: the largest power of two up to 16 bytes dividing both the
+// address and the row length in bytes, so that every row start (and the end
+// of the matrix) falls on a multiple of it.
+int load_unit(const void* p, int64_t len)
+{
+    int u = 16;
+    while (u > 2 && ((((uintptr_t)p) % (uintptr_t)u) != 0 || ((uint64_t)len * 2u) % (uint64_t)u != 0)) u >>= 1;
+    return u;
+}
+
 bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes)
 {
     const uint64_t x = (uint64_t)(uintptr_t)a, y = (uint64_t)(uintptr_t)b;
@@ -415,6 +426,8 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
                      (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 15u) == 0) &&
                      (((uintptr_t)bias & 7u) == 0);
+    p.unit_a = load_unit(A, K);
+    p.unit_b = load_unit(B, N);
     p.tiles_m = (int)cdiv(M, vec ? e.cfg.block_m : e.elem_bm);
     p.tiles_n = (int)cdiv(N, vec ? e.cfg.block_n : e.elem_bn);
     p.group_m = l.group_m;

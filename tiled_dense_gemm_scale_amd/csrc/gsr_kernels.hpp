@@ -57,7 +57,8 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r ^ (r >> 3)) & 7u
 
 // Eight consecutive fp16 values starting at element offset `elem`; the first
 // `nvalid` of them exist (0..8).  The vector form needs nvalid in {0, 8} and
-// a 16-byte aligned address.
+// a 16-byte aligned address; the element form loads the values one by one,
+// each at its own (2-byte aligned) address.
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t rs, uint32_t elem, int nvalid)
 {
@@ -76,6 +77,41 @@ __device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t rs, uint32_t elem,
         v[1] = h[2] | (h[3] << 16);
         v[2] = h[4] | (h[5] << 16);
         v[3] = h[6] | (h[7] << 16);
+        return v;
+    }
+}
+
+// load8 for the element-wise path with the operand's load unit U (16, 8, 4
+// or 2 bytes).  Every row of the operand starts on a multiple of the unit and
+// so does the end of the matrix, and a chunk starts on a multiple of 16 bytes
+// from its row, so each load is naturally aligned and lies wholly inside or
+// wholly outside the records.  Loads that hold no valid value are not issued;
+// values past `nvalid` inside a load (the next row's) are cleared.
+template <int U>
+__device__ __forceinline__ u32x4 load8_unit(__amdgpu_buffer_rsrc_t rs, uint32_t elem, int nvalid)
+{
+    if constexpr (U == 16) {
+        return load8<true>(rs, elem, nvalid);  // nvalid is 0 or 8 with this unit
+    } else if constexpr (U == 2) {
+        return load8<false>(rs, elem, nvalid);
+    } else {
+        const uint32_t off = elem * 2u;
+        u32x4 v;
+        if constexpr (U == 8) {
+            const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rs, nvalid > 0 ? off : kOutOfRange, 0, 0);
+            const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(rs, nvalid > 4 ? off + 8u : kOutOfRange, 0, 0);
+            v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            static_assert(U == 4, "load units of 16, 8, 4 or 2 bytes");
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, nvalid > 2 * i ? off + 4u * (uint32_t)i : kOutOfRange, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (2 * i >= nvalid) v[i] = 0u;
+            else if (2 * i + 1 >= nvalid) v[i] &= 0xffffu;
+        }
         return v;
     }
 }
@@ -109,6 +145,10 @@ struct Problem {
     int tiles_m, tiles_n;
     int group_m;
     int xcd_remap;
+    // the element-wise kernel's load unit per operand, in bytes (16, 8, 4 or
+    // 2): the largest power of two up to 16 that divides both the operand's
+    // address and its row length in bytes (2K for A, 2N for B)
+    int unit_a, unit_b;
 };
 
 // ---- epilogue -----------------------------------------------------------
@@ -298,18 +338,25 @@ gemm_scale_relu_kernel(Problem p)
     u32x4 areg[T::A_PER];
     u32x4 breg[T::B_PER][8];
 
-    auto load_tile = [&](int k0) {
-        {
-            const int kk = k0 + a_kc * 8;
-            const int kval = min(max(p.K - kk, 0), 8);
+    // On the element-wise path each operand is read in the widest unit its
+    // alignment allows (p.unit_a, p.unit_b); the unit is picked once per
+    // K-step (a uniform branch on a kernel argument) for a copy of the load
+    // loop compiled for it, so the loads of a step still issue back to back.
+    // The vector path reads 16-byte units throughout.
+    auto load_a = [&](auto unit_tag, int k0) {
+        constexpr int U = decltype(unit_tag)::value;
+        const int kk = k0 + a_kc * 8;
+        const int kval = min(max(p.K - kk, 0), 8);
 #pragma unroll
-            for (int i = 0; i < T::A_PER; ++i) {
-                const int r = a_r0 + i * A_ROW_STEP;
-                const int m = m0 + r;
-                const int nv = (m < p.M) ? kval : 0;
-                areg[i] = load8<VEC>(ra, (uint32_t)m * (uint32_t)p.K + (uint32_t)kk, nv);
-            }
+        for (int i = 0; i < T::A_PER; ++i) {
+            const int r = a_r0 + i * A_ROW_STEP;
+            const int m = m0 + r;
+            const int nv = (m < p.M) ? kval : 0;
+            areg[i] = load8_unit<U>(ra, (uint32_t)m * (uint32_t)p.K + (uint32_t)kk, nv);
         }
+    };
+    auto load_b = [&](auto unit_tag, int k0) {
+        constexpr int U = decltype(unit_tag)::value;
 #pragma unroll
         for (int i = 0; i < T::B_PER; ++i) {
             const int blk = tid + i * NT;
@@ -321,10 +368,28 @@ gemm_scale_relu_kernel(Problem p)
                 for (int j = 0; j < 8; ++j) {
                     const int k = k0 + kb * 8 + j;
                     const int nv = (k < p.K) ? nval : 0;
-                    breg[i][j] = load8<VEC>(rb, (uint32_t)k * (uint32_t)p.N + (uint32_t)n, nv);
+                    breg[i][j] = load8_unit<U>(rb, (uint32_t)k * (uint32_t)p.N + (uint32_t)n, nv);
                 }
             }
         }
+    };
+    using U16 = std::integral_constant<int, 16>;
+    using U8 = std::integral_constant<int, 8>;
+    using U4 = std::integral_constant<int, 4>;
+    using U2 = std::integral_constant<int, 2>;
+    auto with_unit = [&](int unit, auto&& f) {
+        if constexpr (VEC) {
+            f(U16{});
+        } else {
+            if (unit == 16) f(U16{});
+            else if (unit == 8) f(U8{});
+            else if (unit == 4) f(U4{});
+            else f(U2{});
+        }
+    };
+    auto load_tile = [&](int k0) {
+        with_unit(p.unit_a, [&](auto u) { load_a(u, k0); });
+        with_unit(p.unit_b, [&](auto u) { load_b(u, k0); });
     };
 
     auto store_tile = [&](int stage) {
@@ -415,6 +480,10 @@ gemm_scale_relu_kernel(Problem p)
     // Accumulator block (a, b): lane l holds m = l % 32 and, in register
     // 4g + i, n = 8g + 4*(l/32) + i.
     const float alpha = p.alpha;
+    // four outputs n..n+3 of row m: the element path writes them with the
+    // widest naturally aligned stores their address allows (one of 8 bytes,
+    // two of 4, or 2 + 4 + 2), and one by one at the edge of C
+    const uint32_t c_align = (uint32_t)(uintptr_t)p.C & 7u;
     auto store4 = [&](int m, int n, half4 h) {
         const u32x2 w = __builtin_bit_cast(u32x2, h);
         const uint32_t elem = (uint32_t)m * (uint32_t)p.N + (uint32_t)n;
@@ -422,11 +491,25 @@ gemm_scale_relu_kernel(Problem p)
             const uint32_t off = ((m < p.M) & (n < p.N)) ? elem * 2u : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
         } else {
+            const uint32_t off = elem * 2u, al = (c_align + off) & 7u;
+            if ((m < p.M) & (n + 3 < p.N)) {
+                if (al == 0u) {
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                } else if (al == 4u) {
+                    __builtin_amdgcn_raw_buffer_store_b32(w[0], rc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(w[1], rc, off + 4u, 0, 0);
+                } else {  // 2 mod 4: values 1 and 2 share an aligned dword
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[0] & 0xffffu), rc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32((w[0] >> 16) | (w[1] << 16), rc, off + 2u, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[1] >> 16), rc, off + 6u, 0, 0);
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t off = ((m < p.M) & (n + i < p.N)) ? (elem + i) * 2u : kOutOfRange;
-                const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
-                __builtin_amdgcn_raw_buffer_store_b16(hv, rc, off, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t o = ((m < p.M) & (n + i < p.N)) ? (elem + i) * 2u : kOutOfRange;
+                    const uint16_t hv = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
+                    __builtin_amdgcn_raw_buffer_store_b16(hv, rc, o, 0, 0);
+                }
             }
         }
     };
