@@ -86,10 +86,11 @@ typedef struct gsr_config {
 /* The fused operation (the tutorial's kernel call: A, B, C, scale).
  * M, N, K >= 0.  M == 0 or N == 0: success, nothing enqueued.  K == 0: every
  * output is the empty sum, C is filled with +0.  Any pointer alignment of at
- * least 2 bytes is accepted; 16-byte aligned A, B and C with K and N
- * multiples of 8 take the 128-bit vector path, anything else an element-wise
- * path (a register-staged kernel of the same tile, or of a 64x64 tile for the
- * K-split kinds).  Returns a gsr_status. */
+ * least 2 bytes is accepted; 16-byte aligned A and B with K and N multiples
+ * of 8 take the 128-bit vector path (C written in the widest stores its own
+ * alignment allows), anything else an element-wise path (a register-staged
+ * kernel of the same tile, or of a 64x64 tile for the K-split kinds, reading
+ * each operand in the widest unit its alignment allows).  Returns a gsr_status. */
 int gemm_scale_relu(int64_t M, int64_t N, int64_t K,
                     const void* A, const void* B, void* C,
                     float alpha, void* stream);

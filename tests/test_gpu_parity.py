@@ -243,22 +243,23 @@ def test_empty_outputs(gsr):
 
 
 @pytest.mark.parametrize("cid", [-1, 16, 17, 18, 21, 22, 25, 28, 29, 31, 32])
-def test_c_aligned_to_8_not_16_bytes(gsr, orc, cid):
-    """A and B 16-byte aligned, C only 8-byte aligned (4 elements into a 16-byte
-    aligned buffer): the 128-bit stores need 16-byte aligned rows of C, so
-    this takes the element-wise path, whose grid comes from its own tile.
-    The bands around C stay untouched and every output matches the oracle."""
+@pytest.mark.parametrize("c_off", [4, 2, 1], ids=lambda o: f"C+{2 * o}B")
+def test_c_less_aligned_than_16_bytes(gsr, orc, cid, c_off):
+    """A and B 16-byte aligned with K and N multiples of 8, C only 8-, 4- or
+    2-byte aligned (1, 2 or 4 elements into a 16-byte aligned buffer): the
+    vector kernels run and write C in 8-, 4- or 2-byte stores.  The bands
+    around C stay untouched and every output matches the oracle."""
     M, N, K = 300, 264, 200
     a, b = W.normal_inputs(M, N, K, seed=31)
     ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
-    say(f"[gpu] C at an 8-byte offset, config {cid}")
+    say(f"[gpu] C at a {2 * c_off}-byte offset, config {cid}")
     buf = torch.full((M * N + 64,), 0x7E5A, dtype=torch.int16, device=DEV).view(torch.float16)
     assert buf.data_ptr() % 16 == 0
-    c = buf[4:4 + M * N].view(M, N)
+    c = buf[c_off:c_off + M * N].view(M, N)
     PT.run_gpu(a, b, 0.5, config_id=cid, c=c)
     hb = bits(buf.cpu())
-    assert np.all(hb[:4] == 0x7E5A) and np.all(hb[4 + M * N:] == 0x7E5A)
-    PT.assert_parity(f"C+8 bytes cfg{cid}", hb[4:4 + M * N].reshape(M, N), ref)
+    assert np.all(hb[:c_off] == 0x7E5A) and np.all(hb[c_off + M * N:] == 0x7E5A)
+    PT.assert_parity(f"C+{2 * c_off} bytes cfg{cid}", hb[c_off:c_off + M * N].reshape(M, N), ref)
 
 
 @pytest.mark.parametrize("offset", [1, 2, 3, 4, 8])

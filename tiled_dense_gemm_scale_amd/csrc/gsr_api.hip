@@ -419,13 +419,14 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     p.K = (int)K;
     p.alpha = alpha;
     p.act = (int)activation;
-    // The vector kernels read A and B and write C in 16-byte units (C's rows
-    // start 2N bytes apart, a multiple of 16 when N % 8 == 0) and read the
-    // bias in 8-byte units; anything else takes the element-wise kernel,
-    // whose own tile sets the grid.
+    // The vector kernels read A and B in 16-byte units and the bias in 8-byte
+    // units, and write C in row segments whose starts are 2N bytes apart (a
+    // multiple of 16 when N % 8 == 0), in the widest stores C's own alignment
+    // allows (p.unit_c); anything else takes the element-wise kernel, whose
+    // own tile sets the grid.
     const bool vec = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)A & 15u) == 0) &&
-                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)C & 15u) == 0) &&
-                     (((uintptr_t)bias & 7u) == 0);
+                     (((uintptr_t)B & 15u) == 0) && (((uintptr_t)bias & 7u) == 0);
+    p.unit_c = load_unit(C, N);
     p.unit_a = load_unit(A, K);
     p.unit_b = load_unit(B, N);
     p.tiles_m = (int)cdiv(M, vec ? e.cfg.block_m : e.elem_bm);

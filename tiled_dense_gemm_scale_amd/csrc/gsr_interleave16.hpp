@@ -132,14 +132,19 @@ __device__ __forceinline__ void ilv16_epilogue_t(const Problem& p, const f32x4 (
     // MI355X, same bits: 0.2-2 % faster at 4096^3, 3072^3, 16384^3, the
     // LLM shape and 2048 x 4096 x 4096, in either timing order.
     constexpr int kStoreNonTemporal = 2;
+    // C at a 16-byte aligned address takes one 16-byte store per row segment;
+    // a less aligned C, the stores its alignment allows (p.unit_c)
+    with_store_unit(p.unit_c, [&](auto unit_tag) {
+        constexpr int U = decltype(unit_tag)::value;
 #pragma unroll
-    for (int j = 0; j < (int)(T::WTM / RPI); ++j) {
-        const uint32_t r = RPI * (uint32_t)j + lane / CPR;
-        const u32x4 v = *(const u32x4*)(ep + r * RB + ((sc ^ (r & (CPR - 1u))) << 4));
-        const int m = m0 + wm * T::WTM + (int)r;
-        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, kStoreNonTemporal);
-    }
+        for (int j = 0; j < (int)(T::WTM / RPI); ++j) {
+            const uint32_t r = RPI * (uint32_t)j + lane / CPR;
+            const u32x4 v = *(const u32x4*)(ep + r * RB + ((sc ^ (r & (CPR - 1u))) << 4));
+            const int m = m0 + wm * T::WTM + (int)r;
+            const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * N + (uint32_t)n) * 2u : kOutOfRange;
+            store16_unit<U, kStoreNonTemporal>(v, rc, off);
+        }
+    });
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))

@@ -149,7 +149,46 @@ struct Problem {
     // 2): the largest power of two up to 16 that divides both the operand's
     // address and its row length in bytes (2K for A, 2N for B)
     int unit_a, unit_b;
+    // the vector kernels' store unit for C, in bytes (16, 8, 4 or 2): the
+    // largest power of two up to 16 dividing C's address (their rows of C are
+    // 2N bytes apart, a multiple of 16)
+    int unit_c;
 };
+
+// Eight outputs (16 bytes) at byte offset `off` of C, a multiple of 16 from
+// C's start, written in stores of the launch's unit for C (U = 16, 8, 4 or 2
+// bytes), so each store is naturally aligned.  An out-of-range offset
+// (kOutOfRange and up) drops every part.  AUX is the cache policy.
+template <int U, int AUX>
+__device__ __forceinline__ void store16_unit(u32x4 v, __amdgpu_buffer_rsrc_t rc, uint32_t off)
+{
+    if constexpr (U == 16) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, AUX);
+    } else if constexpr (U == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[0], v[1]}, rc, off, 0, AUX);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[2], v[3]}, rc, off + 8u, 0, AUX);
+    } else if constexpr (U == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(v[i], rc, off + 4u * (uint32_t)i, 0, AUX);
+    } else {
+        static_assert(U == 2, "store units of 16, 8, 4 or 2 bytes");
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xffffu)), rc,
+                                                  off + 2u * (uint32_t)i, 0, AUX);
+    }
+}
+
+// f(integral_constant<int, U>) for the launch's store unit: one uniform
+// branch per store loop, each loop compiled for its unit.
+template <class F>
+__device__ __forceinline__ void with_store_unit(int unit, F&& f)
+{
+    if (unit == 16) f(std::integral_constant<int, 16>{});
+    else if (unit == 8) f(std::integral_constant<int, 8>{});
+    else if (unit == 4) f(std::integral_constant<int, 4>{});
+    else f(std::integral_constant<int, 2>{});
+}
 
 // ---- epilogue -----------------------------------------------------------
 // The tutorial's epilogue is v = alpha * acc, max(v, 0), narrow.  The

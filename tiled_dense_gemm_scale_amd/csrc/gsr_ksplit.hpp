@@ -121,45 +121,48 @@ struct KsSum {
         const float alpha = p.alpha;
         const bool plain = plain_epilogue(p);
         with_activation(p.act, [&](auto act_tag) {
-            constexpr int ACT = decltype(act_tag)::value;
+            with_store_unit(p.unit_c, [&](auto unit_tag) {
+                constexpr int ACT = decltype(act_tag)::value;
+                constexpr int U = decltype(unit_tag)::value;
 #pragma unroll
-            for (int j = 0; j < NU; ++j) {
-                const int u = tid + NT * j;
-                if (UNITS % NT != 0 && u >= UNITS) break;
-                const int mr = u / QN, q = u % QN;
-                f32x4 lo[NW], hi[NW];
+                for (int j = 0; j < NU; ++j) {
+                    const int u = tid + NT * j;
+                    if (UNITS % NT != 0 && u >= UNITS) break;
+                    const int mr = u / QN, q = u % QN;
+                    f32x4 lo[NW], hi[NW];
 #pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    lo[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q));
-                    hi[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q + 1));
-                }
-                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        s0[i] += lo[w][i];
-                        s1[i] += hi[w][i];
+                    for (int w = 0; w < NW; ++w) {
+                        lo[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q));
+                        hi[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q + 1));
                     }
-                }
-                half4 h0, h1;
-                if (plain) {
+                    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v0 = s0[i] * alpha, v1 = s1[i] * alpha;
-                        h0[i] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
-                        h1[i] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
+                    for (int w = 0; w < NW; ++w) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            s0[i] += lo[w][i];
+                            s1[i] += hi[w][i];
+                        }
                     }
-                } else {
-                    h0 = epilogue4<ACT>(s0, alpha, bvs[j][0]);
-                    h1 = epilogue4<ACT>(s1, alpha, bvs[j][1]);
+                    half4 h0, h1;
+                    if (plain) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v0 = s0[i] * alpha, v1 = s1[i] * alpha;
+                            h0[i] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
+                            h1[i] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
+                        }
+                    } else {
+                        h0 = epilogue4<ACT>(s0, alpha, bvs[j][0]);
+                        h1 = epilogue4<ACT>(s1, alpha, bvs[j][1]);
+                    }
+                    const int m = m0 + mr, n = n0 + 8 * q;
+                    const uint32_t off =
+                        ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+                    const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
+                    store16_unit<U, 0>(u32x4{w0[0], w0[1], w1[0], w1[1]}, rc, off);
                 }
-                const int m = m0 + mr, n = n0 + 8 * q;
-                const uint32_t off =
-                    ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-                const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{w0[0], w0[1], w1[0], w1[1]}, rc, off, 0, 0);
-            }
+            });
         });
     }
 };
