@@ -18,7 +18,8 @@
  *
  * Ownership and ordering.  A, B and C are device pointers owned by the caller
  * (any allocation the HIP runtime can address from the current device).  The
- * library allocates nothing and keeps no per-call state; it only enqueues
+ * library allocates nothing and keeps no per-call state (the entry points
+ * with a workspace keep theirs in the caller's workspace); it only enqueues
  * kernels on `stream` (a hipStream_t; NULL means the null stream) and returns
  * before they finish.  The caller synchronises.  Calls are thread-safe.
  *
@@ -138,6 +139,57 @@ int gemm_scale_bias_act_ex(int64_t M, int64_t N, int64_t K,
 int gemm_scale_bias_act_cfg(int64_t M, int64_t N, int64_t K,
                             const void* A, const void* B, const void* bias, void* C,
                             float alpha, int32_t activation, void* stream, const gsr_config* cfg);
+
+/* The same operations with a workspace, so that K can be split across
+ * workgroups.  Split-K is the decomposition the PKUHPC tutorial's page and
+ * the aikraft.ru guide leave open for skinny products (section 3 of the
+ * guide: the schedule depends on the size); here it serves shapes whose
+ * output has too few tiles of the K-split kinds (configurations 21 and 22) to
+ * occupy the chip, such as a few rows against a 4096-wide weight: each tile's
+ * K-steps are cut into `parts` runs, one workgroup each, whose fp32 sums meet
+ * in the workspace, and the workgroup of a tile that finishes last adds them
+ * in part order, applies the epilogue and stores C.  The sum of a part is
+ * that of the unsplit kernel over its K range, so results differ from the
+ * unsplit call only by the order of fp32 additions.
+ *
+ *   workspace  device memory owned by the caller, 16-byte aligned, not
+ *              overlapping A, B, C or the bias.  Its first bytes hold one
+ *              32-bit arrival counter per tile and must be zero before the
+ *              first call (allocate it zero-filled); every call leaves them
+ *              zero again, so the same workspace serves any number of calls
+ *              in stream order.  Calls that may run at the same time (other
+ *              streams, other threads) need workspaces of their own.
+ *   workspace_bytes  its size; gsr_workspace_bytes gives what the library's
+ *              choice needs (at most 4 MiB + 512 bytes for any shape)
+ *   splits     0: the library's choice (shapes of at most 128 such tiles
+ *              and at least 32 K-steps of 128 whose unsplit call would not
+ *              already stream near the read ceiling: up to four parts, at
+ *              most one workgroup per CU and eight K-steps per part; fewer
+ *              parts when the workspace is smaller, none without one);
+ *              n >= 1: at most n parts (never
+ *              more than one per K-step), GSR_ERROR_INVALID_VALUE if the
+ *              workspace cannot hold them, GSR_ERROR_INVALID_CONFIG for n > 1
+ *              with a configuration that cannot split.  1..16.
+ * A call that does not split (other configurations, the element-wise path,
+ * parts = 1) ignores the workspace.  Otherwise as gemm_scale_bias_act_ex and
+ * gemm_scale_relu; GSR_ERROR_INVALID_VALUE also for a misaligned or
+ * overlapping workspace, a negative size or splits outside 0..16. */
+int gemm_scale_bias_act_ws(int64_t M, int64_t N, int64_t K,
+                           const void* A, const void* B, const void* bias, void* C,
+                           float alpha, int32_t activation,
+                           void* workspace, int64_t workspace_bytes,
+                           void* stream, int32_t config_id, int32_t splits);
+
+/* gemm_scale_relu with a workspace: the selector's configuration and the
+ * library's split. */
+int gemm_scale_relu_ws(int64_t M, int64_t N, int64_t K,
+                       const void* A, const void* B, void* C, float alpha,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes the library's split needs for an M x N x K call on the
+ * 128-bit path (the selector's or the tuning table's configuration); 0 when
+ * that call does not split, -1 for a negative dimension.  Host only. */
+int64_t gsr_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Tuning table: exact problem shapes mapped to a launch, consulted before the
  * built-in selector (by every entry point called with config id -1, and by

@@ -243,3 +243,65 @@ def test_binding_rejects_operands_on_different_devices():
         gsr.gemm_scale_relu(T((4, 8), 0), T((8, 4), 0), 0.5, c=T((4, 4), 1))
     with pytest.raises(ValueError, match="A's device"):
         gsr.gemm_scale_bias_act(T((4, 8), 0), T((8, 4), 0), T((4,), 1), c=T((4, 4), 0))
+
+
+# ---- the entry points with a workspace --------------------------------------
+
+WS = FAKE + (1 << 20)  # a workspace address clear of A, B and C
+
+
+@pytest.mark.parametrize("ws,nbytes,splits,status", [
+    (WS + 8, 1 << 16, 0, 1),          # workspace not 16-byte aligned
+    (WS, -1, 0, 1),                   # negative size
+    (FAKE + 8192 - 64, 4096, 0, 1),   # workspace running into C (C: 32 bytes at FAKE + 8192)
+    (FAKE, 4096, 0, 1),               # workspace over A
+    (FAKE + 4096 - 16, 4096, 0, 1),   # ... and over B
+    (WS, 1 << 16, -1, 1),             # splits outside 0..16
+    (WS, 1 << 16, 17, 1),
+])
+def test_workspace_argument_errors(native, ws, nbytes, splits, status):
+    st = native.gemm_scale_bias_act_ws(4, 4, 4, FAKE, FAKE + 4096, 0, FAKE + 8192, 1.0, 0, ws, nbytes, 0, -1,
+                                       splits)
+    assert st == status, (ws, nbytes, splits, st)
+
+
+def test_workspace_entry_points_share_the_checks(native):
+    import math
+    args = (FAKE, FAKE + 4096, 0, FAKE + 8192)
+    assert native.gemm_scale_bias_act_ws(-1, 4, 4, *args, 1.0, 0, WS, 4096, 0, -1, 0) == 1
+    assert native.gemm_scale_bias_act_ws(4, 4, 4, *args, math.nan, 0, WS, 4096, 0, -1, 0) == 1
+    assert native.gemm_scale_bias_act_ws(4, 4, 4, *args, 1.0, 3, WS, 4096, 0, -1, 0) == 1
+    assert native.gemm_scale_bias_act_ws(4, 4, 4, *args, 1.0, 0, WS, 4096, 0, 99, 0) == 6
+    assert native.gemm_scale_bias_act_ws(4, 4, 4, *args, 1.0, 0, WS, 4096, 0, 8, 0) == 6   # a retired id
+    assert native.gemm_scale_bias_act_ws(4, 4, 4, *args, 1.0, 0, WS, 4096, 0, -2, 0) == 6
+    assert native.gemm_scale_bias_act_ws(2 ** 31, 4, 4, *args, 1.0, 0, WS, 4096, 0, -1, 0) == 2
+    assert native.gemm_scale_bias_act_ws(0, 4, 4, 0, 0, 0, 0, 1.0, 0, 0, 0, 0, -1, 0) == 0
+    assert native.gemm_scale_relu_ws(4, 4, 4, FAKE, FAKE + 4096, FAKE + 16, 0.5, WS, 4096, 0) == 1  # C over A
+    assert native.gemm_scale_relu_ws(4, 4, 4, FAKE, FAKE + 4096, FAKE + 8192, 0.5, WS + 4, 4096, 0) == 1
+    assert native.gemm_scale_relu_ws(0, 16, 16, 0, 0, 0, 0.5, 0, 0, 0) == 0
+
+
+def test_workspace_bytes(native):
+    """The library's split (host only): a 32-bit counter per tile in a
+    256-byte-rounded region, then parts x tiles fp32 partial tiles.  Decode
+    shapes against a 4096-wide weight split in four (64 tiles of 32 x 64),
+    two tile rows in two (128 tiles); too few K-steps, too many tiles, or an
+    unsplit call near the read ceiling: none."""
+    tile = 32 * 64 * 4
+    assert native.workspace_bytes(1, 4096, 4096) == 256 + 4 * 64 * tile
+    assert native.workspace_bytes(32, 4096, 11008) == 256 + 4 * 64 * tile
+    assert native.workspace_bytes(64, 4096, 4096) == 512 + 2 * 128 * tile
+    assert native.workspace_bytes(1, 1024, 4096) == 256 + 4 * 16 * tile
+    assert native.workspace_bytes(1, 4096, 2048) == 0          # 16 K-steps
+    assert native.workspace_bytes(1, 11008, 4096) == 0         # 172 tiles
+    assert native.workspace_bytes(1, 8192, 8192) == 0          # unsplit already near the read ceiling
+    assert native.workspace_bytes(1024, 1024, 1024) == 0
+    assert native.workspace_bytes(4096, 4096, 4096) == 0
+    assert native.workspace_bytes(0, 4096, 4096) == 0
+    assert native.workspace_bytes(16, 4096, 0) == 0
+    with pytest.raises(native.GsrError):
+        native.workspace_bytes(-1, 4, 4)
+    # never more than 4 MiB + 512 bytes (at most 256 workgroups of 64 x 64 fp32)
+    worst = max(native.workspace_bytes(M, N, K) for M in (1, 7, 32, 33, 64, 100, 128, 200, 512)
+                for N in (8, 64, 1000, 2048, 4096, 8192) for K in (4096, 8192, 11008, 65536))
+    assert 0 < worst <= (4 << 20) + 512

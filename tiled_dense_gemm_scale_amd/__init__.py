@@ -25,9 +25,10 @@ import torch
 
 from . import _native
 from ._native import (GsrError, clear_tuning, config_ids, get_config, load_tuning, num_configs, select_config,
-                      status_string, tuning_entries, version)
+                      status_string, tuning_entries, version, workspace_bytes)
 
 __all__ = ["gemm_scale_relu", "gemm_scale_relu_ex", "gemm_scale_bias_act", "gemm_launch", "GsrError",
+           "gemm_scale_relu_ws", "gemm_scale_bias_act_ws", "workspace_bytes", "new_workspace",
            "select_config", "get_config", "num_configs", "config_ids", "status_string", "version", "configs",
            "ACTIVATIONS",
            "load_tuning", "clear_tuning", "tuning_entries"]
@@ -107,6 +108,59 @@ def gemm_scale_bias_act(a: torch.Tensor, b: torch.Tensor, bias: Optional[torch.T
         s = _stream_handle(a.device, stream)
         st = _native.gemm_scale_bias_act(M, N, K, a.data_ptr(), b.data_ptr(), bptr, c.data_ptr(), alpha,
                                          ACTIVATIONS[activation], s, config_id)
+    _native.check(st)
+    return c
+
+
+def new_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A zero-filled workspace of `nbytes` bytes (uint8) for the entry points
+    that split K across workgroups.  The kernels leave its counters at zero,
+    so one workspace serves any number of calls in stream order; calls that
+    may overlap need one each."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def _check_workspace(workspace: torch.Tensor, device: torch.device):
+    if (workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda
+            or not workspace.is_contiguous() or workspace.device != device):
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    return workspace.data_ptr(), workspace.numel()
+
+
+def gemm_scale_bias_act_ws(a: torch.Tensor, b: torch.Tensor, workspace: torch.Tensor,
+                           bias: Optional[torch.Tensor] = None, alpha: float = 1.0, activation: str = "relu",
+                           c: Optional[torch.Tensor] = None, stream=None, config_id: int = -1,
+                           splits: int = 0) -> torch.Tensor:
+    """gemm_scale_bias_act with a workspace (see new_workspace), so that K
+    can be split across workgroups: splits 0 is the library's choice, n >= 1
+    at most n parts.  Returns C."""
+    M, N, K, c = _check_operands(a, b, c)
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
+    bptr = 0
+    if bias is not None:
+        if (bias.dtype != torch.float16 or tuple(bias.shape) != (N,) or not bias.is_cuda or not bias.is_contiguous()
+                or bias.device != a.device):
+            raise ValueError(f"bias must be a contiguous ({N},) float16 tensor on A's device")
+        bptr = bias.data_ptr()
+    wptr, wbytes = _check_workspace(workspace, a.device)
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_bias_act_ws(M, N, K, a.data_ptr(), b.data_ptr(), bptr, c.data_ptr(), alpha,
+                                            ACTIVATIONS[activation], wptr, wbytes, s, config_id, splits)
+    _native.check(st)
+    return c
+
+
+def gemm_scale_relu_ws(a: torch.Tensor, b: torch.Tensor, alpha: float, workspace: torch.Tensor,
+                       c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """gemm_scale_relu with a workspace (see new_workspace and
+    workspace_bytes): the library may split K across workgroups.  Returns C."""
+    M, N, K, c = _check_operands(a, b, c)
+    wptr, wbytes = _check_workspace(workspace, a.device)
+    with torch.cuda.device(a.device):
+        s = _stream_handle(a.device, stream)
+        st = _native.gemm_scale_relu_ws(M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), alpha, wptr, wbytes, s)
     _native.check(st)
     return c
 

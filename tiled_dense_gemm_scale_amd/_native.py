@@ -78,6 +78,12 @@ def lib() -> ctypes.CDLL:
             L.gemm_scale_bias_act_cfg.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp,
                                                    ctypes.POINTER(GsrConfig)]
             L.gemm_scale_bias_act_cfg.restype = ctypes.c_int
+            L.gemm_scale_bias_act_ws.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, i64, vp, i32, i32]
+            L.gemm_scale_bias_act_ws.restype = ctypes.c_int
+            L.gemm_scale_relu_ws.argtypes = [i64, i64, i64, vp, vp, vp, f32, vp, i64, vp]
+            L.gemm_scale_relu_ws.restype = ctypes.c_int
+            L.gsr_workspace_bytes.argtypes = [i64, i64, i64]
+            L.gsr_workspace_bytes.restype = i64
             L.gsr_load_tuning.argtypes = [ctypes.c_char_p]
             L.gsr_load_tuning.restype = ctypes.c_int
             L.gsr_clear_tuning.argtypes = []
@@ -137,6 +143,30 @@ def gemm_scale_bias_act_cfg(M: int, N: int, K: int, A: int, B: int, bias: int, C
     cfg.id, cfg.group_m, cfg.xcd_remap = int(config_id), int(group_m), int(xcd_remap)
     return lib().gemm_scale_bias_act_cfg(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
                                          int(activation), stream or None, ctypes.byref(cfg))
+
+
+def gemm_scale_bias_act_ws(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, alpha: float,
+                           activation: int, workspace: int, workspace_bytes: int, stream: int,
+                           config_id: int = -1, splits: int = 0) -> int:
+    """Raw entry point with a workspace (K split across workgroups).
+    Returns the gsr_status."""
+    return lib().gemm_scale_bias_act_ws(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
+                                        int(activation), workspace or None, int(workspace_bytes), stream or None,
+                                        int(config_id), int(splits))
+
+
+def gemm_scale_relu_ws(M: int, N: int, K: int, A: int, B: int, C: int, alpha: float, workspace: int,
+                       workspace_bytes: int, stream: int) -> int:
+    return lib().gemm_scale_relu_ws(M, N, K, A or None, B or None, C or None, float(alpha), workspace or None,
+                                    int(workspace_bytes), stream or None)
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes the library's K split needs for this shape (0: none)."""
+    got = int(lib().gsr_workspace_bytes(int(M), int(N), int(K)))
+    if got < 0:
+        raise GsrError(GSR_ERROR_INVALID_VALUE, status_string(GSR_ERROR_INVALID_VALUE))
+    return got
 
 
 def load_tuning(path: str) -> None:

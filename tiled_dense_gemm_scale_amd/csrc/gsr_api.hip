@@ -73,10 +73,10 @@ hipError_t launch_ksplit(const Problem& p, int grid, hipStream_t s)
     return launch_kernel((gsr::gemm_scale_relu_ksplit_kernel<BM, BN, S>), dim3(grid), dim3(256), s, p);
 }
 
-template <int BM, int BN, int S, int D>
+template <int BM, int BN, int S, int D, bool SPLIT>
 hipError_t launch_kspec(const Problem& p, int grid, hipStream_t s)
 {
-    return launch_kernel((gsr::gemm_scale_relu_kspec_kernel<BM, BN, S, D>), dim3(grid), dim3(512), s, p);
+    return launch_kernel((gsr::gemm_scale_relu_kspec_kernel<BM, BN, S, D, SPLIT>), dim3(grid), dim3(512), s, p);
 }
 
 struct Entry {
@@ -84,6 +84,7 @@ struct Entry {
     launch_fn vec;       // 128-bit path (16-byte aligned A, B and C, K and N multiples of 8)
     launch_fn elem;      // element-wise path, any 2-byte aligned layout
     int elem_bm, elem_bn;  // the output tile of the element-wise kernel (its grid)
+    launch_fn split;     // 128-bit path with K split across workgroups (a workspace), or null
 };
 
 // Four waves splitting K inside the workgroup (block_k = 128 per step, waves
@@ -93,16 +94,17 @@ struct Entry {
     Entry                                                                                             \
     {                                                                                                 \
         {ID, BM, BN, 128, 1, 1, S, GROUP, 1, gsr::KsCfg<BM, BN, S>::LDS_BYTES},                       \
-            launch_ksplit<BM, BN, S>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64                  \
+            launch_ksplit<BM, BN, S>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64, nullptr         \
     }
 
 // As GSR_KSPLIT with four more waves that only issue the copies, DEPTH steps
-// ahead.
+// ahead; with a workspace, the same kernel can also split K across workgroups.
 #define GSR_KSPEC(ID, BM, BN, S, D, GROUP)                                                            \
     Entry                                                                                             \
     {                                                                                                 \
         {ID, BM, BN, 128, 1, 1, S, GROUP, 1, gsr::KsCfg<BM, BN, S>::LDS_BYTES},                       \
-            launch_kspec<BM, BN, S, D>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64                \
+            launch_kspec<BM, BN, S, D, false>, launch_staged<64, 64, 64, 2, 2, false>, 64, 64,        \
+            launch_kspec<BM, BN, S, D, true>                                                          \
     }
 
 // An explicitly interleaved kernel (stages 1: two LDS buffers per operand, or
@@ -111,7 +113,8 @@ struct Entry {
 #define GSR_ILV(ID, BM, BN, STAGES, LDS, FN, XCD)                                                          \
     Entry                                                                                                 \
     {                                                                                                     \
-        {ID, BM, BN, 64, 2, 2, STAGES, 4, XCD, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN    \
+        {ID, BM, BN, 64, 2, 2, STAGES, 4, XCD, LDS}, FN, launch_staged<BM, BN, 64, 2, 2, false>, BM, BN,   \
+            nullptr                                                                                       \
     }
 
 // The compiled tile table, by id.  Ids are stable from one library version to
@@ -217,6 +220,66 @@ int select(int64_t M, int64_t N, int64_t K)
         }
     }
     return best;
+}
+
+// ---- K split across workgroups ---------------------------------------------
+// The copy-wave K-split tiles (configurations 21 and 22) cover few outputs, so
+// shapes with few tiles (decode shapes: a handful of rows against a 4096-wide
+// weight) leave most CUs idle while each workgroup streams its whole K range.
+// With a workspace the K range of every tile is cut into `parts` runs of
+// K-steps, one workgroup each; the parts' fp32 sums meet in the workspace and
+// the workgroup of a tile that finishes last adds them (gsr_ksplit.hpp).
+// Workspace layout: one 32-bit arrival counter per tile (a region rounded up
+// to 256 bytes), then parts x tiles partial tiles of bm x bn fp32, row-major.
+constexpr int kSplitStep = 128;    // K-step of the K-split kernels
+constexpr int kSplitMaxParts = 16;
+
+struct SplitPlan {
+    int parts;       // 1: no split
+    int64_t kchunk;  // K values per part (a multiple of kSplitStep)
+    int64_t bytes;   // workspace the plan needs
+};
+
+int64_t split_count_bytes(int64_t tiles) { return (4 * tiles + 255) / 256 * 256; }
+
+// `want` parts of a tile's K-steps (at most one part per K-step), no part
+// empty.
+SplitPlan split_plan(int64_t tiles, int bm, int bn, int64_t K, int want)
+{
+    const int64_t steps = cdiv(K, kSplitStep);
+    int64_t parts = std::min<int64_t>(want, steps);
+    if (parts <= 1) return SplitPlan{1, K, 0};
+    const int64_t per = cdiv(steps, parts);
+    parts = cdiv(steps, per);
+    if (parts <= 1) return SplitPlan{1, K, 0};
+    return SplitPlan{(int)parts, per * kSplitStep,
+                     split_count_bytes(tiles) + parts * tiles * (int64_t)bm * bn * 4};
+}
+
+// The library's split.  Timed on one MI355X with the 32x64 tile against the
+// unsplit kernel (graph replays, 2..16 parts): a part costs about 0.31 us
+// per K-step of 128 plus about 1 us per call, and a split adds 2.5-5 us of
+// its own (each part's pipeline fill, the partial sums' round trip), so
+//  * it pays only from 32 K-steps (K = 4096: 1x4096x4096 11.1 -> 7.8 us,
+//    1x2048x4096 9.4 -> 7.2, 8x4096x4096 11.5 -> 8.3; K = 11008:
+//    1x4096x11008 28.0 -> 17.7, 16x2048x11008 29.5 -> 13.3; at K = 2048 and
+//    1024 it lost 3-30 %);
+//  * up to four parts, never more workgroups than CUs (two workgroups of
+//    these tiles do not fit one CU: 1024^3 in 512 workgroups took 16 us
+//    instead of 6); eight parts were slower than four at 16 and 32 tiles;
+//  * with 65-128 tiles, two parts gained where the unsplit call streams well
+//    below the part's read ceiling (48x4096x4096 12.9 -> 11.0 us,
+//    64x4096x11008 30.7 -> 23.4) and lost 7-10 % where it is near it
+//    (1x8192x4096, 16x8192x8192: ~6 TB/s unsplit), so no split when the
+//    unsplit call's estimated rate exceeds 4 TB/s.
+int split_parts_for(int64_t M, int64_t N, int64_t K, int64_t tiles)
+{
+    const int64_t steps = cdiv(K, kSplitStep);
+    if (steps < 32 || tiles > 128 || tiles <= 0) return 1;
+    const double est_us = 1.0 + 0.31 * (double)steps;
+    const double bytes = 2.0 * ((double)M * K + (double)K * N + (double)M * N);
+    if (bytes / (est_us * 1e-6) > 4e12) return 1;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({4, 256 / tiles, steps / 8}));
 }
 
 // ---- tuning table: exact shapes -> launch choice ---------------------------
@@ -379,8 +442,13 @@ namespace {
 
 // Checks, then the launch.  `forced` >= 0 is a config id, -1 the selector,
 // -2 the launch in `given`.
+// `splits` < 0: no workspace (the entry points without one); 0: the
+// library's split when the configuration supports one and the workspace
+// holds it (fewer parts until it does); >= 1: that many parts at most, and
+// the workspace must hold them.
 int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, float alpha,
-        int32_t activation, void* stream, int forced, const Launch& given)
+        int32_t activation, void* stream, int forced, const Launch& given, void* workspace = nullptr,
+        int64_t workspace_bytes = 0, int splits = -1)
 {
     int st = validate(M, N, K, A, B, C);
     if (st != GSR_SUCCESS) return st;
@@ -394,6 +462,18 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     }
     if (forced < -2 || (forced >= 0 && entry_of(forced) == nullptr)) return GSR_ERROR_INVALID_CONFIG;
     if (forced == -2 && !valid_launch(given)) return GSR_ERROR_INVALID_CONFIG;
+    if (splits > kSplitMaxParts) return GSR_ERROR_INVALID_VALUE;
+    if (splits >= 0 && workspace_bytes < 0) return GSR_ERROR_INVALID_VALUE;
+    if (splits >= 0 && workspace != nullptr) {
+        // written while A, B and the bias are read and C is written
+        if ((uintptr_t)workspace & 15u) return GSR_ERROR_INVALID_VALUE;
+        const uint64_t wb = (uint64_t)workspace_bytes;
+        if (overlaps(workspace, wb, A, (uint64_t)M * (uint64_t)K * 2u) ||
+            overlaps(workspace, wb, B, (uint64_t)K * (uint64_t)N * 2u) ||
+            overlaps(workspace, wb, C, (uint64_t)M * (uint64_t)N * 2u) ||
+            (bias != nullptr && overlaps(workspace, wb, bias, (uint64_t)N * 2u)))
+            return GSR_ERROR_INVALID_VALUE;
+    }
     if (M == 0 || N == 0) return GSR_SUCCESS;
     st = check_device();
     if (st != GSR_SUCCESS) return st;
@@ -433,8 +513,33 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     p.tiles_n = (int)cdiv(N, vec ? e.cfg.block_n : e.elem_bn);
     p.group_m = l.group_m;
     p.xcd_remap = l.xcd_remap;
-    const int grid = p.tiles_m * p.tiles_n;
-    const hipError_t err = (vec ? e.vec : e.elem)(p, grid, s);
+    p.ksplit = 1;
+    p.kchunk = (int)K;
+    p.ws_part = nullptr;
+    p.ws_count = nullptr;
+    const int tiles = p.tiles_m * p.tiles_n;
+    SplitPlan plan{1, K, 0};
+    if (splits > 1 && !(vec && e.split != nullptr)) {
+        // a forced split that this configuration or layout cannot run
+        if (e.split == nullptr) return GSR_ERROR_INVALID_CONFIG;
+    } else if (splits >= 0 && vec && e.split != nullptr) {
+        const int want = splits > 0 ? splits : split_parts_for(M, N, K, tiles);
+        plan = split_plan(tiles, e.cfg.block_m, e.cfg.block_n, K, want);
+        if (plan.parts > 1 && (workspace == nullptr || workspace_bytes < plan.bytes)) {
+            if (splits > 0) return GSR_ERROR_INVALID_VALUE;  // the workspace cannot hold the forced split
+            while (plan.parts > 1 && (workspace == nullptr || workspace_bytes < plan.bytes))
+                plan = split_plan(tiles, e.cfg.block_m, e.cfg.block_n, K, plan.parts - 1);
+        }
+    }
+    if (plan.parts > 1) {
+        p.ksplit = plan.parts;
+        p.kchunk = (int)plan.kchunk;
+        p.ws_count = (uint32_t*)workspace;
+        p.ws_part = (float*)((uint8_t*)workspace + split_count_bytes(tiles));
+        const hipError_t err = e.split(p, tiles * plan.parts, s);
+        return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
+    }
+    const hipError_t err = (vec ? e.vec : e.elem)(p, tiles, s);
     return err == hipSuccess ? GSR_SUCCESS : GSR_ERROR_LAUNCH;
 }
 
@@ -524,6 +629,34 @@ int gemm_scale_relu(int64_t M, int64_t N, int64_t K, const void* A, const void* 
                     void* stream)
 {
     return gemm_scale_bias_act_ex(M, N, K, A, B, nullptr, C, alpha, GSR_ACT_RELU, stream, -1);
+}
+
+int gemm_scale_bias_act_ws(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                           void* C, float alpha, int32_t activation, void* workspace, int64_t workspace_bytes,
+                           void* stream, int32_t config_id, int32_t splits)
+{
+    if (config_id < -1) return GSR_ERROR_INVALID_CONFIG;
+    if (splits < 0) return GSR_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, B, bias, C, alpha, activation, stream, config_id, Launch{0, 0, 0}, workspace,
+               workspace_bytes, splits);
+}
+
+int gemm_scale_relu_ws(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, float alpha,
+                       void* workspace, int64_t workspace_bytes, void* stream)
+{
+    return gemm_scale_bias_act_ws(M, N, K, A, B, nullptr, C, alpha, GSR_ACT_RELU, workspace, workspace_bytes,
+                                  stream, -1, 0);
+}
+
+int64_t gsr_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    const Launch l = resolve(M, N, K, -1);
+    const Entry& e = *entry_of(l.id);
+    if (e.split == nullptr) return 0;
+    const int64_t tiles = cdiv(M, e.cfg.block_m) * cdiv(N, e.cfg.block_n);
+    return split_plan(tiles, e.cfg.block_m, e.cfg.block_n, K, split_parts_for(M, N, K, tiles)).bytes;
 }
 
 }  // extern "C"

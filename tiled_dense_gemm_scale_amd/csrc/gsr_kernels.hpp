@@ -153,6 +153,13 @@ struct Problem {
     // largest power of two up to 16 dividing C's address (their rows of C are
     // 2N bytes apart, a multiple of 16)
     int unit_c;
+    // K split across workgroups (the copy-wave K-split kernels with a
+    // workspace): ksplit parts of kchunk K values each (a multiple of the
+    // kernel's K-step; the last part ends at K), the parts' fp32 sums and the
+    // tiles' arrival counters in the caller's workspace.  ksplit 1: none.
+    int ksplit, kchunk;
+    float* ws_part;
+    uint32_t* ws_count;
 };
 
 // Eight outputs (16 bytes) at byte offset `off` of C, a multiple of 16 from

@@ -34,7 +34,7 @@
 
 namespace gsr {
 
-template <int BM, int BN, int STAGES, int DEPTH>
+template <int BM, int BN, int STAGES, int DEPTH, bool SPLIT>
 __global__ void __launch_bounds__(512)
 gemm_scale_relu_kspec_kernel(Problem p)
 {
@@ -50,10 +50,20 @@ gemm_scale_relu_kspec_kernel(Problem p)
     const bool copier = wave8 >= NW;  // waves 4..7 copy, 0..3 multiply
     const int wave = wave8 & (NW - 1);
 
+    // SPLIT: workgroup id = part * tiles + tile; part j covers K values
+    // [j * kchunk, min(K, (j + 1) * kchunk))
+    int tile = blockIdx.x, part = 0, kbeg = 0, kend = p.K;
+    if constexpr (SPLIT) {
+        const int tiles = p.tiles_m * p.tiles_n;
+        part = blockIdx.x / tiles;
+        tile = blockIdx.x - part * tiles;
+        kbeg = part * p.kchunk;
+        kend = min(p.K, kbeg + p.kchunk);
+    }
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, p, tm, tn);
+    tile_of(tile, SPLIT ? p.tiles_m * p.tiles_n : (int)gridDim.x, p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int ksteps = (p.K + BK - 1) / BK;
+    const int ksteps = (kend - kbeg + BK - 1) / BK;
 
     using Sum = KsSum<BM, BN, NW, 512>;  // the cross-wave sum runs on all eight waves
     static_assert(Sum::BYTES <= T::LDS_BYTES, "partial tiles fit in LDS");
@@ -75,7 +85,7 @@ gemm_scale_relu_kspec_kernel(Problem p)
             const int m = m0 + r;
             a_ok[i] = m < p.M;
             a_k[i] = 8 * c;
-            a_off[i] = ((uint32_t)m * (uint32_t)p.K + (uint32_t)(8 * c)) * 2u;
+            a_off[i] = ((uint32_t)m * (uint32_t)p.K + (uint32_t)(kbeg + 8 * c)) * 2u;
         }
         uint32_t b_off[T::B_PER];
         int b_k[T::B_PER];
@@ -88,19 +98,21 @@ gemm_scale_relu_kspec_kernel(Problem p)
             const int n = n0 + 8 * c;
             b_ok[i] = n < p.N;
             b_k[i] = k;
-            b_off[i] = ((uint32_t)k * (uint32_t)p.N + (uint32_t)n) * 2u;
+            b_off[i] = ((uint32_t)(kbeg + k) * (uint32_t)p.N + (uint32_t)n) * 2u;
         }
+        // k0: offset of the step from the part's first K value
+        const int klen = kend - kbeg;
         auto issue = [&](int stage, int k0) {
             const uint32_t As = lds0 + stage * T::STAGE_BYTES;
             const uint32_t Bs = As + T::A_BYTES;
 #pragma unroll
             for (int i = 0; i < T::A_PER; ++i) {
-                const bool ok = a_ok[i] & (k0 + a_k[i] < p.K);
+                const bool ok = a_ok[i] & (k0 + a_k[i] < klen);
                 copy16_to_lds(ra, ok ? a_off[i] + (uint32_t)k0 * 2u : kOutOfRange, As + (wave + i * NW) * 1024);
             }
 #pragma unroll
             for (int i = 0; i < T::B_PER; ++i) {
-                const bool ok = b_ok[i] & (k0 + b_k[i] < p.K);
+                const bool ok = b_ok[i] & (k0 + b_k[i] < klen);
                 copy16_to_lds(rb, ok ? b_off[i] + (uint32_t)k0 * (uint32_t)p.N * 2u : kOutOfRange,
                               Bs + (wave + i * NW) * 1024);
             }
@@ -212,6 +224,13 @@ gemm_scale_relu_kspec_kernel(Problem p)
     lds_barrier();  // partial tiles written
 
     // ---- every wave: sum, epilogue, one 16-byte store per unit --------------------
+    if constexpr (SPLIT) {
+        __shared__ int last;
+        if (p.ksplit > 1) {
+            Sum::split_sum_store(p, smem, &last, tid, m0, n0, bvs, tile, part);
+            return;
+        }
+    }
     Sum::sum_store(p, smem, tid, m0, n0, bvs);
 }
 

@@ -114,11 +114,59 @@ struct KsSum {
                 }
     }
 
+    // unit u's eight outputs summed over the waves' partial tiles, in wave
+    // order, starting from +0
+    struct Sums {
+        f32x4 lo, hi;
+    };
+    __device__ static Sums unit_sum(const uint8_t* smem, int u)
+    {
+        const int mr = u / QN, q = u % QN;
+        f32x4 lo[NW], hi[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            lo[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q));
+            hi[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q + 1));
+        }
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0[i] += lo[w][i];
+                s1[i] += hi[w][i];
+            }
+        }
+        return Sums{s0, s1};
+    }
+
+    // the epilogue of one unit's eight sums and its store to C
+    template <int ACT, int U>
+    __device__ static void finish(const Problem& p, __amdgpu_buffer_rsrc_t rc, bool plain, f32x4 s0, f32x4 s1,
+                                  const f32x4 (&bv)[2], int m, int n)
+    {
+        const float alpha = p.alpha;
+        half4 h0, h1;
+        if (plain) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v0 = s0[i] * alpha, v1 = s1[i] * alpha;
+                h0[i] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
+                h1[i] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
+            }
+        } else {
+            h0 = epilogue4<ACT>(s0, alpha, bv[0]);
+            h1 = epilogue4<ACT>(s1, alpha, bv[1]);
+        }
+        const uint32_t off = ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
+        const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
+        store16_unit<U, 0>(u32x4{w0[0], w0[1], w1[0], w1[1]}, rc, off);
+    }
+
     __device__ static void sum_store(const Problem& p, const uint8_t* smem, int tid, int m0, int n0,
                                      const f32x4 (&bvs)[NU][2])
     {
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
-        const float alpha = p.alpha;
         const bool plain = plain_epilogue(p);
         with_activation(p.act, [&](auto act_tag) {
             with_store_unit(p.unit_c, [&](auto unit_tag) {
@@ -128,42 +176,94 @@ struct KsSum {
                 for (int j = 0; j < NU; ++j) {
                     const int u = tid + NT * j;
                     if (UNITS % NT != 0 && u >= UNITS) break;
-                    const int mr = u / QN, q = u % QN;
-                    f32x4 lo[NW], hi[NW];
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        lo[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q));
-                        hi[w] = *(const f32x4*)(smem + addr(w, mr, 2 * q + 1));
-                    }
-                    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            s0[i] += lo[w][i];
-                            s1[i] += hi[w][i];
-                        }
-                    }
-                    half4 h0, h1;
-                    if (plain) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float v0 = s0[i] * alpha, v1 = s1[i] * alpha;
-                            h0[i] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
-                            h1[i] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
-                        }
-                    } else {
-                        h0 = epilogue4<ACT>(s0, alpha, bvs[j][0]);
-                        h1 = epilogue4<ACT>(s1, alpha, bvs[j][1]);
-                    }
-                    const int m = m0 + mr, n = n0 + 8 * q;
-                    const uint32_t off =
-                        ((m < p.M) & (n < p.N)) ? ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * 2u : kOutOfRange;
-                    const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
-                    store16_unit<U, 0>(u32x4{w0[0], w0[1], w1[0], w1[1]}, rc, off);
+                    const Sums t = unit_sum(smem, u);
+                    finish<ACT, U>(p, rc, plain, t.lo, t.hi, bvs[j], m0 + u / QN, n0 + 8 * (u % QN));
                 }
             });
         });
+    }
+
+    // The same sum when the tile's K range is split over p.ksplit
+    // workgroups (part `part` of tile `tile` here).  Each workgroup writes its
+    // fp32 sums to its slot of the workspace's partial tiles and counts
+    // itself in the tile's arrival counter; the workgroup that arrives last
+    // adds the parts in part order (0, 1, ..., starting from +0, its own sums
+    // standing in for its slot), so the result does not depend on the
+    // arrival order, runs the epilogue, stores C and puts the counter back to
+    // zero for the next call.  No workgroup waits for another.
+    //
+    // The workgroups of a tile may run on different XCDs, whose L2 caches
+    // are not coherent with each other.  The partial sums are therefore
+    // written and read with device-scope accesses (relaxed atomics at agent
+    // scope: stores that write through the L2, loads that do not take a
+    // possibly stale L2 line), each wave waits until its stores have
+    // completed before the workgroup barrier that precedes the count, and the
+    // last workgroup reads only after its count has returned.  Release and
+    // acquire fences at agent scope would order the same accesses, but they
+    // write back and invalidate the whole L2: timed with them, every
+    // workgroup added about 0.2 us, serialised per XCD.
+    __device__ static void split_sum_store(const Problem& p, const uint8_t* smem, int* flag, int tid, int m0, int n0,
+                                           const f32x4 (&bvs)[NU][2], int tile, int part)
+    {
+        static_assert(NU == 1, "one sum unit per thread");
+        const int tiles = p.tiles_m * p.tiles_n, parts = p.ksplit;
+        const int u = tid;
+        const int m = m0 + u / QN, n = n0 + 8 * (u % QN);
+        const bool live = (UNITS % NT == 0 || u < UNITS) && (m < p.M) && (n < p.N);
+        // the unit's eight sums of part g: four 64-bit words
+        const size_t slot = (size_t)tile * (BM * BN) + (size_t)u * 8, stride = (size_t)tiles * (BM * BN);
+        auto words = [&](int g) { return (uint64_t*)(p.ws_part + (slot + (size_t)g * stride)); };
+        Sums own{};
+        if (live) {
+            own = unit_sum(smem, u);
+            const u32x4 lo = __builtin_bit_cast(u32x4, own.lo), hi = __builtin_bit_cast(u32x4, own.hi);
+            uint64_t* dst = words(part);
+            const uint64_t w[4] = {lo[0] | (uint64_t)lo[1] << 32, lo[2] | (uint64_t)lo[3] << 32,
+                                   hi[0] | (uint64_t)hi[1] << 32, hi[2] | (uint64_t)hi[3] << 32};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __hip_atomic_store(dst + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmcnt<0>();  // this wave's partial sums have reached device scope
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(p.ws_count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = (int)(before == (uint32_t)(parts - 1));
+        }
+        __syncthreads();
+        if (*flag == 0) return;
+
+        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            for (int g = 0; g < parts; ++g) {
+                f32x4 v0 = own.lo, v1 = own.hi;
+                if (g != part) {
+                    const uint64_t* src = words(g);
+                    uint64_t w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v0 = __builtin_bit_cast(f32x4, u32x4{(uint32_t)w[0], (uint32_t)(w[0] >> 32), (uint32_t)w[1], (uint32_t)(w[1] >> 32)});
+                    v1 = __builtin_bit_cast(f32x4, u32x4{(uint32_t)w[2], (uint32_t)(w[2] >> 32), (uint32_t)w[3], (uint32_t)(w[3] >> 32)});
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    t0[i] += v0[i];
+                    t1[i] += v1[i];
+                }
+            }
+        }
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C, (uint32_t)p.M * (uint32_t)p.N * 2u);
+        const bool plain = plain_epilogue(p);
+        const f32x4 b0 = bvs[0][0], b1 = bvs[0][1];
+        with_activation(p.act, [&](auto act_tag) {
+            with_store_unit(p.unit_c, [&](auto unit_tag) {
+                constexpr int ACT = decltype(act_tag)::value;
+                constexpr int U = decltype(unit_tag)::value;
+                const f32x4 bv[2] = {b0, b1};
+                // a unit outside C gets an out-of-range offset and stores nothing
+                finish<ACT, U>(p, rc, plain, t0, t1, bv, live ? m : p.M, n);
+            });
+        });
+        if (tid == 0) __hip_atomic_store(p.ws_count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 };
 
