@@ -186,6 +186,27 @@ int gemm_scale_relu_ws(int64_t M, int64_t N, int64_t K,
                        const void* A, const void* B, void* C, float alpha,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gemm_scale_bias_act_ws with the workspace taken from a scratch array that
+ * the library keeps in every device's memory (4 MiB + 512 bytes per device,
+ * present from the time the library's code object is loaded until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current).  The call itself allocates nothing.  Every call
+ * on one device shares that device's array: calls that may overlap on one
+ * device (other streams, other threads, other libraries' copies excepted)
+ * race, and their results and the array's arrival counters are then
+ * undefined.  Calls in stream order are safe: the counters start at zero and
+ * every call leaves them zero.  A split that needs more than the array holds
+ * (only a forced `splits` can) is GSR_ERROR_TOO_LARGE, with nothing
+ * enqueued; the library's own choice always fits.  GSR_ERROR_LAUNCH also
+ * when the runtime cannot give the array's address.  Otherwise as
+ * gemm_scale_bias_act_ws. */
+int gemm_scale_bias_act_noalloc(int64_t M, int64_t N, int64_t K,
+                                const void* A, const void* B, const void* bias, void* C,
+                                float alpha, int32_t activation,
+                                void* stream, int32_t config_id, int32_t splits);
+
 /* Workspace bytes the library's split needs for an M x N x K call on the
  * 128-bit path (the selector's or the tuning table's configuration); 0 when
  * that call does not split, -1 for a negative dimension.  Host only. */

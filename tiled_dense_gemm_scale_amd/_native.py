@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
             L.gemm_scale_bias_act_ws.restype = ctypes.c_int
             L.gemm_scale_relu_ws.argtypes = [i64, i64, i64, vp, vp, vp, f32, vp, i64, vp]
             L.gemm_scale_relu_ws.restype = ctypes.c_int
+            L.gemm_scale_bias_act_noalloc.argtypes = [i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, i32, i32]
+            L.gemm_scale_bias_act_noalloc.restype = ctypes.c_int
             L.gsr_workspace_bytes.argtypes = [i64, i64, i64]
             L.gsr_workspace_bytes.restype = i64
             L.gsr_load_tuning.argtypes = [ctypes.c_char_p]
@@ -159,6 +161,14 @@ def gemm_scale_relu_ws(M: int, N: int, K: int, A: int, B: int, C: int, alpha: fl
                        workspace_bytes: int, stream: int) -> int:
     return lib().gemm_scale_relu_ws(M, N, K, A or None, B or None, C or None, float(alpha), workspace or None,
                                     int(workspace_bytes), stream or None)
+
+
+def gemm_scale_bias_act_noalloc(M: int, N: int, K: int, A: int, B: int, bias: int, C: int, alpha: float,
+                                activation: int, stream: int, config_id: int = -1, splits: int = 0) -> int:
+    """Raw entry point that allocates nothing: the K split's workspace is
+    the library's per-device scratch array.  Returns the gsr_status."""
+    return lib().gemm_scale_bias_act_noalloc(M, N, K, A or None, B or None, bias or None, C or None, float(alpha),
+                                             int(activation), stream or None, int(config_id), int(splits))
 
 
 def workspace_bytes(M: int, N: int, K: int) -> int:

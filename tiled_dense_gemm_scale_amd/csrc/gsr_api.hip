@@ -21,6 +21,17 @@
 #include "gsr_interleave16d.hpp"
 #include "gsr_interleave16c.hpp"
 
+// ---- scratch of the allocation-free entry point ---------------------------------
+// gemm_scale_bias_act_noalloc takes the K split's workspace from this array
+// instead of an argument: every device the library runs on holds its own
+// copy from the time the code object is loaded until the process ends.  It
+// is zero-filled at load (uninitialised device data), and the split kernels
+// put the arrival counters at its start back to zero at the end of every
+// call.  Host code uses the per-device address that hipGetSymbolAddress
+// gives, never the array's name, which on the host is only a stand-in.
+constexpr int64_t kScratchBytes = (4 << 20) + 512;  // the largest split the library picks: 256 parts of 64x64 fp32 + counters
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 using gsr::Problem;
@@ -353,6 +364,34 @@ int check_device()
     return GSR_SUCCESS;
 }
 
+// The scratch array's address on the current device, looked up once per
+// device (with that device current) on its first use.
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_status[kMaxDevices];
+
+int scratch_of_current_device(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GSR_ERROR_NO_DEVICE;
+    }
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            g_scratch_status[dev] = GSR_ERROR_LAUNCH;
+        } else {
+            g_scratch_ptr[dev] = ptr;
+            g_scratch_status[dev] = GSR_SUCCESS;
+        }
+    });
+    *out = g_scratch_ptr[dev];
+    return g_scratch_status[dev];
+}
+
 // The element-wise kernel's load unit for an operand whose rows are `len`
 // fp16 values long: the largest power of two up to 16 bytes dividing both the
 // address and the row length in bytes, so that every row start (and the end
@@ -445,10 +484,11 @@ namespace {
 // `splits` < 0: no workspace (the entry points without one); 0: the
 // library's split when the configuration supports one and the workspace
 // holds it (fewer parts until it does); >= 1: that many parts at most, and
-// the workspace must hold them.
+// the workspace must hold them.  `use_scratch`: the workspace is this
+// device's scratch array, and a split it cannot hold is GSR_ERROR_TOO_LARGE.
 int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias, void* C, float alpha,
         int32_t activation, void* stream, int forced, const Launch& given, void* workspace = nullptr,
-        int64_t workspace_bytes = 0, int splits = -1)
+        int64_t workspace_bytes = 0, int splits = -1, bool use_scratch = false)
 {
     int st = validate(M, N, K, A, B, C);
     if (st != GSR_SUCCESS) return st;
@@ -477,6 +517,11 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
     if (M == 0 || N == 0) return GSR_SUCCESS;
     st = check_device();
     if (st != GSR_SUCCESS) return st;
+    if (use_scratch) {
+        st = scratch_of_current_device(&workspace);
+        if (st != GSR_SUCCESS) return st;
+        workspace_bytes = kScratchBytes;
+    }
     hipStream_t s = (hipStream_t)stream;
 
     if (K == 0) {
@@ -526,6 +571,7 @@ int run(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const voi
         const int want = splits > 0 ? splits : split_parts_for(M, N, K, tiles);
         plan = split_plan(tiles, e.cfg.block_m, e.cfg.block_n, K, want);
         if (plan.parts > 1 && (workspace == nullptr || workspace_bytes < plan.bytes)) {
+            if (use_scratch) return GSR_ERROR_TOO_LARGE;      // beyond the scratch array
             if (splits > 0) return GSR_ERROR_INVALID_VALUE;  // the workspace cannot hold the forced split
             while (plan.parts > 1 && (workspace == nullptr || workspace_bytes < plan.bytes))
                 plan = split_plan(tiles, e.cfg.block_m, e.cfg.block_n, K, plan.parts - 1);
@@ -646,6 +692,16 @@ int gemm_scale_relu_ws(int64_t M, int64_t N, int64_t K, const void* A, const voi
 {
     return gemm_scale_bias_act_ws(M, N, K, A, B, nullptr, C, alpha, GSR_ACT_RELU, workspace, workspace_bytes,
                                   stream, -1, 0);
+}
+
+int gemm_scale_bias_act_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const void* bias,
+                                void* C, float alpha, int32_t activation, void* stream, int32_t config_id,
+                                int32_t splits)
+{
+    if (config_id < -1) return GSR_ERROR_INVALID_CONFIG;
+    if (splits < 0) return GSR_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, B, bias, C, alpha, activation, stream, config_id, Launch{0, 0, 0}, nullptr, 0, splits,
+               true);
 }
 
 int64_t gsr_workspace_bytes(int64_t M, int64_t N, int64_t K)
