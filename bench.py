@@ -292,6 +292,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--config-id", type=int, default=-1, help="force a tile configuration")
+    ap.add_argument("--workspace", action="store_true",
+                    help="call the entry point with a workspace (K split across workgroups where the "
+                         "library picks one), with the bytes gsr_workspace_bytes gives")
     ap.add_argument("--epilogue", choices=sorted(EPILOGUES), default="relu",
                     help="relu: the tutorial's C = ReLU(alpha A B); the others time the epilogue variants "
                          "C = act(alpha A B + bias) (bias: seeded N(0,1) fp16 per column)")
@@ -360,8 +363,16 @@ def main(argv=None) -> int:
     bias_cpu = W.bias_input(w.N) if has_bias else None
     bias = bias_cpu.to(dev) if has_bias else None
 
+    ws, ws_bytes = None, None
+    if args.workspace:
+        ws_bytes = gsr.workspace_bytes(w.M, w.N, w.K)
+        ws = gsr.new_workspace(ws_bytes, device=dev)
+        log(f"[bench] workspace {ws_bytes} bytes ({'K split across workgroups' if ws_bytes else 'no split'})")
+
     def step():
-        if args.epilogue == "relu":
+        if ws is not None:
+            gsr.gemm_scale_bias_act_ws(a, b, ws, bias, w.alpha, act, c=c, stream=stream, config_id=args.config_id)
+        elif args.epilogue == "relu":
             gsr.gemm_scale_relu_ex(a, b, w.alpha, args.config_id, c=c, stream=stream)
         else:
             gsr.gemm_scale_bias_act(a, b, bias, w.alpha, act, c=c, stream=stream, config_id=args.config_id)
@@ -552,7 +563,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 2} bytes read, {n * 2} bytes written")
 
-    roofline = roofline_of(w, ms, load_traffic(w.name, w.flops))
+    # the committed traffic records are of the unsplit kernels
+    split = bool(ws_bytes)
+    roofline = roofline_of(w, ms, None if split else load_traffic(w.name, w.flops))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)")
@@ -582,6 +595,7 @@ def main(argv=None) -> int:
             "tile": {k: cfg[k] for k in ("id", "block_m", "block_n", "block_k", "waves_m", "waves_n", "group_m",
                                          "xcd_remap")},
             "tuning": os.path.relpath(args.tuning, ROOT) if args.tuning else None,
+            "workspace_bytes": ws_bytes,
             "pct_of_peak": round(100 * tflops / PEAK_FP16_TFLOPS, 2),
             "hbm_gbs_algorithmic": round(w.algorithmic_bytes / (ms * 1e-3) / 1e9, 1),
             "device": {"cus": dinfo.get("cus"), "max_clock_mhz": (dinfo["clock_khz"] / 1000.0) if "clock_khz" in dinfo else None,

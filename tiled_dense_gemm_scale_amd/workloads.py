@@ -77,8 +77,15 @@ COLSHARD8 = Workload("llm_mlp_colshard8_4097x1376x4096", 4097, 1376, 4096, 1.0, 
 MID = Workload("mid_1024x4096x4096", 1024, 4096, 4096, 1.0, 4096 ** -0.5, False,
                "a 1024-row batch against 4096x4096 weights, A ~ N(0,1), B ~ N(0,1/K), alpha=1.0")
 
+# A 16-token decode batch against the MLP down-projection (11008 -> 4096): 64
+# output tiles of 32x64 against 86 K-steps of 128, the class that splits K
+# across workgroups when the call has a workspace.
+DECODE_DOWN = Workload("decode_down_16x4096x11008", 16, 4096, 11008, 1.0, 11008 ** -0.5, False,
+                       "decode batch of 16 tokens against the 4096x11008 MLP down-projection weights, "
+                       "A ~ N(0,1), B ~ N(0,1/K), alpha=1.0")
+
 # Shapes timed and tested besides the five workloads above.
-EXTRA: Dict[str, Workload] = {w.name: w for w in [SKINNY, COLSHARD8, MID]}
+EXTRA: Dict[str, Workload] = {w.name: w for w in [SKINNY, COLSHARD8, MID, DECODE_DOWN]}
 
 
 def by_name(name: str) -> Workload:
