@@ -28,6 +28,12 @@
 // row's eight consecutive outputs and stores them with one 16-byte store;
 // eight lanes cover a 128-byte row of a 64-wide tile, so the stores write
 // whole lines instead of 16-byte pieces of 32 rows.
+//
+// SPLIT (the entry points with a workspace): the K range of every tile is
+// cut into p.ksplit runs of p.kchunk values, one workgroup each (workgroup
+// id = part * tiles + tile), so shapes with few tiles still give every CU a
+// workgroup.  A part runs the same K-steps over its own range; its sums then
+// meet the other parts' in the workspace (KsSum::split_sum_store).
 #pragma once
 
 #include "gsr_ksplit.hpp"
