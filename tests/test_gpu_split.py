@@ -212,3 +212,34 @@ def test_split_on_two_streams(gsr, orc):
         torch.cuda.synchronize()
         for i in range(2):
             PT.assert_parity(f"stream {i} rep {rep}", bits(outs[i].cpu()), refs[i])
+
+
+def _random_split_cases(n=12, seed=2024):
+    """Seeded ragged shapes on the 128-bit path (N and K multiples of 8) with a
+    random part count and K-split tile."""
+    import random
+    rng = random.Random(seed)
+    cases = []
+    for _ in range(n):
+        M = rng.randint(1, 100)
+        N = 8 * rng.randint(1, 150)
+        K = 8 * rng.randint(1, 400)
+        cases.append((M, N, K, rng.choice((21, 22)), rng.randint(2, 16)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_split_cases(), ids=lambda c: "x".join(map(str, c[:3])) + f"-c{c[3]}-p{c[4]}")
+def test_random_shapes_forced_parts_bitwise(gsr, orc, case):
+    """Integer inputs (exact fp32 sums): the split call gives the oracle's bits
+    on seeded ragged shapes, whatever the part count (1 part when K has fewer
+    K-steps than parts asked for collapses them)."""
+    M, N, K, cid, parts = case
+    a, b = W.integer_inputs(M, N, K, seed=M + N + K)
+    alpha = -0.5 if parts % 3 == 0 else 0.5
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), alpha)
+    ws = gsr.new_workspace(16 << 20)
+    say(f"[gpu] split random {case}")
+    c = gsr.gemm_scale_bias_act_ws(a.to(DEV), b.to(DEV), ws, alpha=alpha, config_id=cid, splits=parts)
+    torch.cuda.synchronize()
+    PT.assert_bitwise(f"split random {case}", bits(c.cpu()), ref)
+    assert counters_zero(ws, tiles_of(gsr, M, N, cid))
