@@ -563,9 +563,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {n * 2} bytes read, {n * 2} bytes written")
 
-    # the committed traffic records are of the unsplit kernels
+    # a call that splits K across workgroups runs another kernel: its own record
     split = bool(ws_bytes)
-    roofline = roofline_of(w, ms, None if split else load_traffic(w.name, w.flops))
+    roofline = roofline_of(w, ms, load_traffic(w.name + ("_split" if split else ""), w.flops))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)")
