@@ -192,7 +192,8 @@ int gemm_scale_relu_ws(int64_t M, int64_t N, int64_t K,
  * the library keeps in every device's memory (4 MiB + 512 bytes per device,
  * present from the time the library's code object is loaded until the
  * process ends; its address is looked up once per device, on the first call
- * with that device current).  The call itself allocates nothing.  Every call
+ * with that device current, so under graph capture make one call outside
+ * the capture first).  The call itself allocates nothing.  Every call
  * on one device shares that device's array: calls that may overlap on one
  * device (other streams, other threads, other libraries' copies excepted)
  * race, and their results and the array's arrival counters are then

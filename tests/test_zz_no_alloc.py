@@ -78,3 +78,46 @@ def test_noalloc_rejects_a_split_beyond_its_scratch(native, orc):
     torch.cuda.synchronize()
     ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
     PT.assert_parity("noalloc 512^2x4096 four parts", bits(c.cpu()), ref)
+
+
+def test_noalloc_under_graph_capture(native, orc):
+    """The callers it is for include code under HIP graph capture: after one
+    call outside capture (which looks the scratch array's address up), a
+    captured split call replays with the eager call's bits, eager work in
+    between, and a bias + GELU variant too."""
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    M, N, K = 8, 4096, 4096
+    a, b = W.normal_inputs(M, N, K, seed=9, b_std=K ** -0.5)
+    g = torch.Generator().manual_seed(10)
+    bias = torch.randn(N, generator=g).half()
+    ad, bd, biasd = a.to(DEV), b.to(DEV), bias.to(DEV)
+    assert native.workspace_bytes(M, N, K) > 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = {}
+    for act in (0, 1):  # ReLU without a bias, GELU with one
+        bp = biasd.data_ptr() if act else 0
+        eager = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        c = torch.empty_like(eager)
+        with torch.cuda.stream(s):
+            assert native.gemm_scale_bias_act_noalloc(M, N, K, ad.data_ptr(), bd.data_ptr(), bp, eager.data_ptr(),
+                                                      1.0, act, s.cuda_stream, -1, 0) == 0
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            assert native.gemm_scale_bias_act_noalloc(M, N, K, ad.data_ptr(), bd.data_ptr(), bp, c.data_ptr(),
+                                                      1.0, act, s.cuda_stream, -1, 0) == 0
+        print(f"[gpu] noalloc graph replays, activation {act}", flush=True)
+        for i in range(4):
+            c.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), (act, i)
+            _ = (ad.float() * 2).sum()
+            torch.cuda.synchronize()
+        outs[act] = eager
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 1.0)
+    PT.assert_parity("noalloc relu", bits(outs[0].cpu()), ref)
+    ref, _ = orc.gemm_bias_act(bits(a), bits(b), bits(bias), 1.0, 1)
+    PT.assert_parity("noalloc bias+gelu", bits(outs[1].cpu()), ref)
