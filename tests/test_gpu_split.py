@@ -243,3 +243,22 @@ def test_random_shapes_forced_parts_bitwise(gsr, orc, case):
     torch.cuda.synchronize()
     PT.assert_bitwise(f"split random {case}", bits(c.cpu()), ref)
     assert counters_zero(ws, tiles_of(gsr, M, N, cid))
+
+
+@pytest.mark.parametrize("c_off", [1, 2, 4], ids=lambda o: f"c+{2 * o}B")
+def test_split_with_a_less_aligned_c(gsr, orc, c_off):
+    """C at a 2-, 4- or 8-byte offset keeps the split on the 128-bit path and
+    is written in stores of the size its alignment allows."""
+    M, N, K = 5, 2048, 4096
+    assert gsr.workspace_bytes(M, N, K) > 0
+    a, b = W.integer_inputs(M, N, K, seed=91)
+    ref, _ = orc.gemm_scale_relu(bits(a), bits(b), 0.5)
+    buf = torch.full((M * N + 16,), 3.0, dtype=torch.float16, device=DEV)
+    c = buf[c_off:c_off + M * N].view(M, N)
+    ws = gsr.new_workspace(gsr.workspace_bytes(M, N, K))
+    say(f"[gpu] split with C at +{2 * c_off} bytes")
+    gsr.gemm_scale_relu_ws(a.to(DEV), b.to(DEV), 0.5, ws, c=c)
+    torch.cuda.synchronize()
+    PT.assert_bitwise(f"split C+{2 * c_off}B", bits(c.cpu()), ref)
+    host = buf.cpu()
+    assert bool((host[:c_off] == 3.0).all()) and bool((host[c_off + M * N:] == 3.0).all()), "guard values written"
