@@ -141,11 +141,14 @@ int gemm_scale_bias_act_cfg(int64_t M, int64_t N, int64_t K,
                             float alpha, int32_t activation, void* stream, const gsr_config* cfg);
 
 /* The same operations with a workspace, so that K can be split across
- * workgroups.  Split-K is the decomposition the PKUHPC tutorial's page and
- * the aikraft.ru guide leave open for skinny products (section 3 of the
- * guide: the schedule depends on the size); here it serves shapes whose
- * output has too few tiles of the K-split kinds (configurations 21 and 22) to
- * occupy the chip, such as a few rows against a 4096-wide weight: each tile's
+ * workgroups.  The pages do not describe splitting K: the sum is still the
+ * one the PKUHPC tutorial defines (section 3 display formula), taken over
+ * runs of K and added, and the context is the aikraft.ru guide's section 3
+ * (no schedule is best for every size) and the TileKernels article's section
+ * one (memory bandwidth utilisation as the measure of a memory-bound
+ * product).  It serves shapes whose output has too few tiles of the K-split
+ * kinds (configurations 21 and 22) to occupy the chip, such as a few rows
+ * against a 4096-wide weight: each tile's
  * K-steps are cut into `parts` runs, one workgroup each, whose fp32 sums meet
  * in the workspace, and the workgroup of a tile that finishes last adds them
  * in part order, applies the epilogue and stores C.  The sum of a part is
