@@ -104,6 +104,45 @@ def test_workload_sampled(gsr, orc, name):
     assert 0.45 < zf < 0.55, zf
 
 
+def test_square_16384_every_output_periodic_inputs(gsr, orc):
+    """16384^3 in the selector's launch (the benchmark's), every output bit
+    for bit.  With the periodic integer inputs A[m,k] = ((7m + 13k) mod 9) - 4
+    and B[k,n] = ((5k + 11n) mod 7) - 3, row m of A depends only on m mod 9
+    and column n of B only on n mod 7, so C[m,n] is one of 63 values, chosen
+    by (m mod 9, n mod 7); the oracle computes those 63 (every fp32 partial
+    sum is an exact integer), and each of the 2^28 outputs must equal its
+    class's value.  alpha = 0.5 and -0.5, so the classes with negative sums
+    are seen too."""
+    w = W.WORKLOADS["square_16384"]
+    M, N, K = w.M, w.N, w.K
+    a, b = W.pattern_inputs(M, N, K, device=DEV)
+    a9 = bits(a[:9].cpu())
+    b7 = bits(b[:, :7].contiguous().cpu())
+    ms = np.repeat(np.arange(9, dtype=np.int64), 7)
+    ns = np.tile(np.arange(7, dtype=np.int64), 9)
+    ncls = torch.arange(N, device=DEV) % 7
+    for alpha in (0.5, -0.5):
+        say(f"[gpu] square_16384 periodic integer inputs, alpha={alpha}, selector, every output")
+        c = gsr.gemm_scale_relu(a, b, alpha)
+        torch.cuda.synchronize()
+        ref, _ = orc.gemm_scale_relu_points(a9, b7, alpha, ms, ns)
+        assert len(set(int(v) for v in ref)) >= 5, "the classes should differ"
+        table = torch.from_numpy(np.asarray(ref, dtype=np.uint16).reshape(9, 7).view(np.int16).copy()).to(DEV)
+        got = c.view(torch.int16)
+        for r0 in range(0, M, 1024):
+            rows = torch.arange(r0, min(M, r0 + 1024), device=DEV) % 9
+            bad = got[r0:r0 + rows.numel()] != table[rows][:, ncls]
+            if bool(bad.any()):
+                i, j = (int(x) for x in torch.nonzero(bad)[0])
+                i += r0
+                raise AssertionError(f"16384^3 periodic, alpha={alpha}: output ({i},{j}) is "
+                                     f"0x{int(got[i, j]) & 0xffff:04x}, its class ({i % 9},{j % 7}) gives "
+                                     f"0x{int(table[i % 9, j % 7]) & 0xffff:04x}")
+        del c, got
+    del a, b
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------
 # every tile configuration, several tiles and ragged tails
 # --------------------------------------------------------------------------
